@@ -1,0 +1,98 @@
+"""SIP (sampling with inclusion-probability weighting) in fp64.  TEST INFRASTRUCTURE ONLY.
+
+[hamidun, "three techniques in AB-Attention", SIP paragraph]: a KV block joins
+the sample with probability proportional to its score; the most important
+blocks are always taken and every other block keeps a non-zero chance; each
+chosen block is weighted by the inverse of its inclusion probability (a block
+taken with p = 25% counts four times), which is the Horvitz-Thompson
+estimator and leaves both the softmax numerator and its normaliser unbiased;
+the result is ordinary softmax attention on shifted logits, so no correction
+pass is needed. [edumints, "three innovations", SIP item] says the same.
+
+Readings where the pages are silent:
+  * probabilities p_j = min(1, c * s_j) with c chosen so that sum_j p_j equals
+    the budget K (KV blocks per query block); blocks whose p reaches 1 are the
+    "always taken" ones. c is found by capped water-filling, in fixed point so
+    that every sum is exact and independent of summation order:
+      q_j = floor(s_j * 2^52) as an integer (s_j is the fp32 score in [0, 1],
+      and the row of scores sums to at most 2, so sum q_j < 2^53);
+      U = all blocks, t = 0; repeat:
+        if K - t >= |U|: p = 1 on U, stop;
+        S = sum_{U} q_j; if S == 0: p = (K - t)/|U| on U, stop;
+        c = (K - t) / S  (IEEE double division);
+        Z = {j in U : c * q_j >= 1} (IEEE double product);
+        if Z is empty: p_j = c * q_j on U, stop;
+        p = 1 on Z, t += |Z|, U -= Z.
+  * sampling design = Poisson: one independent Bernoulli(p_j) per block, so
+    the count per row varies around K; the draw uses one uniform
+    u = Philox4x32-10(key = (seed_lo, seed_hi), counter = (j, r, h, b)),
+    u = ((x0 << 32 | x1) >> 11) * 2^-53, and keeps block j iff u < p_j;
+  * the Horvitz-Thompson weight 1/p enters as the logit offset
+    logw = -ln(p) (natural log, fp64, rounded to fp32; +0 for p = 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .philox import philox4x32_10
+
+TWO52 = float(2 ** 52)
+
+
+def fixed_point_scores(s32: np.ndarray) -> np.ndarray:
+    """q_j = floor(s_j * 2^52) for fp32 scores in [0, 1], as uint64."""
+    s = np.asarray(s32, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(s)) or np.any(s < 0.0) or np.any(s > 1.0):
+        raise ValueError("scores must lie in [0, 1]")
+    return np.floor(s * TWO52).astype(np.uint64)
+
+
+def sip_probabilities(s32: np.ndarray, budget: int) -> np.ndarray:
+    """Capped inclusion probabilities of one row; returns float64 [M]."""
+    q = fixed_point_scores(s32)
+    M = q.shape[0]
+    if not 1 <= budget <= M:
+        raise ValueError("budget must lie in [1, M]")
+    if int(q.sum(dtype=np.uint64)) >= 2 ** 53:
+        raise ValueError("a row of scores must sum to less than 2")
+    p = np.zeros(M, dtype=np.float64)
+    active = np.ones(M, dtype=bool)
+    taken = 0
+    while True:
+        n_active = int(active.sum())
+        left = budget - taken
+        if left >= n_active:
+            p[active] = 1.0
+            return p
+        S = int(q[active].sum(dtype=np.uint64))
+        if S == 0:
+            p[active] = float(left) / float(n_active)
+            return p
+        c = float(left) / float(S)
+        act_idx = np.nonzero(active)[0]
+        prod = c * q[act_idx].astype(np.float64)
+        capped = prod >= 1.0
+        if not capped.any():
+            p[act_idx] = prod
+            return p
+        hit = act_idx[capped]
+        p[hit] = 1.0
+        active[hit] = False
+        taken += int(hit.size)
+
+
+def sip_uniforms(seed: int, b: int, h: int, r: int, M: int) -> np.ndarray:
+    """u_j in [0, 1) for j < M from Philox4x32-10, key = seed, counter = (j, r, h, b)."""
+    j = np.arange(M, dtype=np.uint64)
+    x0, x1, _, _ = philox4x32_10(j, r, h, b, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    u53 = ((x0 << np.uint64(32)) | x1) >> np.uint64(11)
+    return u53.astype(np.float64) * (2.0 ** -53)
+
+
+def sip_draw_row(p: np.ndarray, seed: int, b: int, h: int, r: int):
+    """Poisson draw of one row: ascending kept block indices, fp32 log-weights, p."""
+    u = sip_uniforms(seed, b, h, r, p.shape[0])
+    keep = np.nonzero(u < p)[0]
+    pk = p[keep]
+    logw = np.where(pk == 1.0, 0.0, -np.log(pk)).astype(np.float32)
+    return keep.astype(np.int32), logw, pk
