@@ -1,0 +1,183 @@
+/*
+ * absa.h - AB-Attention sampled block-sparse attention for AMD MI355X (gfx950).
+ *
+ * The method (AB-Attention) is described by two web pages:
+ *   [edumints]  edumints blog, "AB-Attention: Video Difuzyon Transformer'larini
+ *               Hizlandirmak Icin Dogru Blok Dikkat Mekanizmasi", sections
+ *               "attention bottleneck" and "three innovations";
+ *   [hamidun]   hamidun news, "AB-Attention speeds up video generation up to
+ *               2.23x and skips 92% of attention compute" (Arabic), section
+ *               "three techniques in AB-Attention" with its IBCS, SIP and
+ *               kernel paragraphs.
+ *
+ * Per (batch b, head h, query block r) the library
+ *   1. averages the 4 keys of every KV block                 [hamidun, IBCS]
+ *   2. clusters the 128 queries of the block into C weighted
+ *      centroids with a fixed number of Lloyd iterations, in
+ *      the original token order                              [hamidun, IBCS;
+ *                                                             edumints, IBCS]
+ *   3. scores every KV block by the weighted softmax attention
+ *      of the centroids toward its mean key                  [hamidun, IBCS]
+ *   4. sets inclusion probabilities proportional to score,
+ *      capped at 1 and summing to the budget, draws blocks
+ *      with Philox4x32-10 and keeps -ln(p) as a logit offset [hamidun, SIP]
+ *   5. runs softmax attention over the gathered 4-token blocks
+ *      with the offsets added to the logits                  [hamidun, SIP and
+ *                                                             kernel paragraphs]
+ * Steps 1-4 build a plan, which the pages rebuild once every 4 denoising steps
+ * and reuse in between [hamidun, kernel paragraph]; step 5 runs every step.
+ * A dense flash-attention kernel from the same code is the comparator.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are device pointers owned by the caller, contiguous
+ *     [B, H, N, d] row-major, element type given by absa_dtype. Outputs have
+ *     the inputs' dtype.
+ *   - Supported shapes: d in {64, 128}; N a multiple of 4 with
+ *     4 <= N <= 2^21; B, H >= 1 with B*H*ceil(N/128) < 2^31.
+ *   - Work is queued on the given HIP stream (NULL = the null stream) and
+ *     returns at once, except absa_plan_create / absa_plan_from_scores /
+ *     absa_plan_import (which block until the plan is built) and the
+ *     export calls (which copy to host memory).
+ *   - Arguments are validated before any HIP call; a rejected call touches
+ *     no device state. No C++ exception crosses this interface.
+ *   - On failure a call returns a non-zero absa_status and records a detail
+ *     message readable through absa_last_error() on the same thread.
+ *   - Plans are immutable after creation and may be shared by concurrent
+ *     attention calls; the caller must not destroy a plan while work that
+ *     uses it is in flight.
+ */
+#ifndef ABSA_H
+#define ABSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum absa_status {
+    ABSA_OK = 0,
+    ABSA_ERR_INVALID_ARG = 1,   /* null pointer, value out of range, bad scores */
+    ABSA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement  */
+    ABSA_ERR_OUT_OF_MEMORY = 3, /* device allocation failed                     */
+    ABSA_ERR_DEVICE = 4,        /* a HIP call failed                            */
+    ABSA_ERR_PLAN_MISMATCH = 5  /* plan built for another (B, H, N, d)          */
+} absa_status;
+
+typedef enum absa_dtype {
+    ABSA_BF16 = 0,              /* bfloat16 storage; MFMA inputs as stored         */
+    ABSA_F32 = 1                /* float32 storage; rounded to bf16 for the MFMA   */
+} absa_dtype;
+
+typedef struct absa_plan_s* absa_plan;
+
+/* Plan parameters. query_block must be 128 and kv_block 4 (the sizes the
+ * pages give: [hamidun, IBCS paragraph] 128-query blocks, [hamidun, kernel
+ * paragraph] KV blocks of at most 4 tokens). n_clusters in [1, 16]
+ * (pages: 8); kmeans_iters in [1, 64] (pages: a fixed count, not stated;
+ * default 4). budget_blocks = K, the KV blocks each query block samples in
+ * expectation, in [1, N/4]. seed = the sampler's 64-bit Philox key; a plan
+ * rebuilt at a later step takes a new seed. keep_intermediates != 0 keeps
+ * the mean keys, centroids, weights and scores on the device for
+ * absa_plan_export_intermediate; otherwise they are freed when the plan is
+ * built. */
+typedef struct absa_plan_params {
+    int32_t query_block;
+    int32_t kv_block;
+    int32_t n_clusters;
+    int32_t kmeans_iters;
+    int64_t budget_blocks;
+    uint64_t seed;
+    int32_t keep_intermediates;
+    int32_t reserved;           /* must be 0 */
+} absa_plan_params;
+
+/* Which retained intermediate absa_plan_export_intermediate copies. */
+typedef enum absa_intermediate {
+    ABSA_INTER_MEAN_KEYS = 0,   /* float [B, H, M, d], M = N/4                   */
+    ABSA_INTER_CENTROIDS = 1,   /* float [B, H, QB, C, d], QB = ceil(N/128)       */
+    ABSA_INTER_WEIGHTS = 2,     /* float [B, H, QB, C]                            */
+    ABSA_INTER_SCORES = 3       /* float [B, H, QB, M]                            */
+} absa_intermediate;
+
+/* Fill *out with the defaults: 128, 4, 8 clusters, 4 iterations, budget 1,
+ * seed 0, keep_intermediates 0. Returns ABSA_ERR_INVALID_ARG on NULL. */
+absa_status absa_plan_params_init(absa_plan_params* out);
+
+/* Build a plan from Q and K: mean keys, IBCS k-means and scores, then SIP
+ * probabilities, Philox draws and HT log-weights (steps 1-4 above).
+ * q, k: device [B, H, N, d] of dtype. On success *out owns device memory
+ * until absa_plan_destroy. Blocks until the plan is complete (one
+ * device-to-host read of the sampled block count sizes the plan). */
+absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype,
+                             int64_t B, int64_t H, int64_t N, int64_t d,
+                             const absa_plan_params* params, void* hip_stream,
+                             absa_plan* out);
+
+/* Build a plan from caller-supplied IBCS scores (SIP only, step 4).
+ * scores_dev: device float [B, H, QB, M]; every score must lie in [0, 1] and
+ * every row must sum to less than 2, else ABSA_ERR_INVALID_ARG (checked on
+ * the device, reported when the call returns). Given the same fp32 scores
+ * and seed, the plan (row pointers, indices, p) is bit-identical to the
+ * documented fixed-point rule. Blocks like absa_plan_create. */
+absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
+                                  int64_t N, int64_t d, int64_t budget_blocks,
+                                  uint64_t seed, void* hip_stream, absa_plan* out);
+
+/* Build a plan from a host CSR: rowptr int64 [rows+1] (rowptr[0] = 0,
+ * non-decreasing), idx int32 [nnz] strictly ascending within each row and in
+ * [0, M), logw float [nnz] finite, p double [nnz] or NULL (then stored as
+ * exp(-logw)). rows = B*H*ceil(N/128). The arrays are copied; the caller
+ * keeps ownership. Blocks until the copy is done. */
+absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx,
+                             const float* logw, const double* p,
+                             int64_t B, int64_t H, int64_t N, int64_t d,
+                             void* hip_stream, absa_plan* out);
+
+/* Shape of a plan; any output pointer may be NULL. shape4 receives
+ * (B, H, N, d). */
+absa_status absa_plan_info(absa_plan plan, int64_t* shape4, int64_t* rows,
+                           int64_t* M, int64_t* nnz);
+
+/* Copy the plan to host buffers sized from absa_plan_info: rowptr [rows+1],
+ * idx [nnz], logw [nnz], p [nnz]; any pointer may be NULL. Synchronous. */
+absa_status absa_plan_export(absa_plan plan, int64_t* rowptr, int32_t* idx,
+                             float* logw, double* p);
+
+/* Copy count elements starting at element offset of a retained intermediate
+ * (see absa_intermediate) to host memory. ABSA_ERR_INVALID_ARG if the plan
+ * did not keep intermediates or the range is out of bounds. Synchronous. */
+absa_status absa_plan_export_intermediate(absa_plan plan, absa_intermediate which,
+                                          int64_t offset, int64_t count, float* dst);
+
+/* Gathered block-sparse attention (step 5): for every query of row (b,h,r),
+ * softmax over the keys of the plan's KV blocks of that row with logit
+ * z = q.k / sqrt(d) + logw(block), times V. o: device [B, H, N, d] of
+ * dtype. A row whose plan holds no block gets zeros. bf16 MFMA products,
+ * fp32 accumulation and softmax. ABSA_ERR_PLAN_MISMATCH if the plan's
+ * (B, H, N, d) differ. */
+absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k,
+                                  const void* v, void* o, absa_dtype dtype,
+                                  int64_t B, int64_t H, int64_t N, int64_t d,
+                                  void* hip_stream);
+
+/* Dense softmax(Q K^T / sqrt(d)) V with the same tiles and arithmetic as
+ * absa_sparse_attention (the comparator). */
+absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
+                                 absa_dtype dtype, int64_t B, int64_t H, int64_t N,
+                                 int64_t d, void* hip_stream);
+
+/* Free a plan (NULL is a no-op). Waits for the device to finish with it. */
+void absa_plan_destroy(absa_plan plan);
+
+/* Static name of a status code. */
+const char* absa_status_string(absa_status status);
+
+/* Detail message of the last failed call on this thread ("" if none). */
+const char* absa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABSA_H */

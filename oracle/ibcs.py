@@ -44,14 +44,18 @@ def mean_keys(K: np.ndarray, kv_block: int = 4) -> np.ndarray:
     return total / kv_block
 
 
-def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4):
+def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4,
+                 return_margin: bool = False):
     """Lloyd k-means on the queries of one query block, in their original order.
 
     Qr: [n, d] float64 (n >= 1). Returns (centroids [C, d], weights [C],
     assignment [n]) where C = n_clusters; clusters beyond C_eff = min(C, n)
     are zero with weight 0. Weights are the clusters' shares of the block's
     queries under the last assignment, and the centroids are the means of
-    that same assignment.
+    that same assignment. With return_margin, a fourth value gives the
+    smallest relative gap (second-nearest minus nearest, over nearest) seen
+    in any assignment step: a gap near rounding level marks a decision that
+    another summation order may take the other way.
     """
     n, d = Qr.shape
     if n < 1 or iters < 1 or n_clusters < 1:
@@ -60,10 +64,15 @@ def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4):
     start = [(m * n) // c_eff for m in range(c_eff)]
     cent = Qr[start].copy()
     assign = np.zeros(n, dtype=np.int64)
+    margin = np.inf
     for _ in range(iters):
         diff = Qr[:, None, :] - cent[None, :, :]           # [n, C_eff, d]
         dist2 = np.einsum("ncd,ncd->nc", diff, diff)
         assign = np.argmin(dist2, axis=1)                  # first minimum wins
+        if return_margin and c_eff > 1:
+            srt = np.sort(dist2, axis=1)
+            gap = (srt[:, 1] - srt[:, 0]) / np.maximum(srt[:, 0], 1e-300)
+            margin = min(margin, float(gap.min()))
         for m in range(c_eff):
             members = assign == m
             cnt = int(members.sum())
@@ -74,6 +83,8 @@ def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4):
     centroids[:c_eff] = cent
     weights = np.zeros(n_clusters)
     weights[:c_eff] = counts / n
+    if return_margin:
+        return centroids, weights, assign, margin
     return centroids, weights, assign
 
 

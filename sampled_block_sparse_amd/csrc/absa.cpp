@@ -1,0 +1,480 @@
+// Host side of the C interface declared in include/absa.h: argument
+// validation (before any HIP call), the plan object, allocation and the
+// launch sequence of the plan and attention kernels.
+#include "absa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "absa_internal.h"
+
+using namespace absa;
+
+struct absa_plan_s {
+    int64_t B = 0, H = 0, N = 0, d = 0, M = 0, QB = 0, rows = 0, nnz = 0;
+    int32_t n_clusters = 0;
+    int64_t* rowptr = nullptr;   // device [rows+1]
+    int32_t* idx = nullptr;      // device [nnz]
+    float* logw = nullptr;       // device [nnz]
+    double* p = nullptr;         // device [nnz]
+    // retained intermediates (keep_intermediates), device
+    float* kbar = nullptr;
+    float* cent = nullptr;
+    float* w = nullptr;
+    float* scores = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+absa_status fail(absa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+absa_status hip_fail(hipError_t e, const char* what) {
+    const absa_status st = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+                               ? ABSA_ERR_OUT_OF_MEMORY
+                               : ABSA_ERR_DEVICE;
+    return fail(st, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+#define ABSA_HIP(call, what)                               \
+    do {                                                   \
+        hipError_t e_ = (call);                            \
+        if (e_ != hipSuccess) return hip_fail(e_, (what)); \
+    } while (0)
+
+// Allocation failure can be forced for tests: ABSA_FAULT_INJECT=alloc.
+bool inject_alloc_failure() {
+    const char* v = std::getenv("ABSA_FAULT_INJECT");
+    return v && std::strcmp(v, "alloc") == 0;
+}
+
+// Device buffers owned until release() hands them over.
+struct DeviceArena {
+    std::vector<void*> ptrs;
+    ~DeviceArena() {
+        for (void* p : ptrs) (void)hipFree(p);
+    }
+    template <typename T>
+    absa_status alloc(T** out, int64_t count, const char* what) {
+        *out = nullptr;
+        if (count <= 0) return ABSA_OK;
+        if (inject_alloc_failure())
+            return fail(ABSA_ERR_OUT_OF_MEMORY, "%s: allocation failure injected", what);
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, static_cast<size_t>(count) * sizeof(T));
+        if (e != hipSuccess) return hip_fail(e, what);
+        ptrs.push_back(p);
+        *out = static_cast<T*>(p);
+        return ABSA_OK;
+    }
+    void release(const void* p) {
+        for (auto& q : ptrs)
+            if (q == p) q = nullptr;
+    }
+};
+
+#define ABSA_TRY(expr)                       \
+    do {                                     \
+        absa_status s_ = (expr);             \
+        if (s_ != ABSA_OK) return s_;        \
+    } while (0)
+
+absa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
+    if (B < 1 || H < 1) return fail(ABSA_ERR_INVALID_ARG, "B and H must be >= 1 (got %lld, %lld)",
+                                    (long long)B, (long long)H);
+    if (N < 4 || N > (int64_t(1) << 21))
+        return fail(ABSA_ERR_UNSUPPORTED, "N must lie in [4, 2^21] (got %lld)", (long long)N);
+    if (N % kKvBlock != 0)
+        return fail(ABSA_ERR_UNSUPPORTED, "N must be a multiple of the KV block size 4 (got %lld)",
+                    (long long)N);
+    if (d != 64 && d != 128)
+        return fail(ABSA_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %lld)", (long long)d);
+    const int64_t QB = (N + kQueryBlock - 1) / kQueryBlock;
+    if (B > (int64_t(1) << 31) / H || B * H > (int64_t(1) << 31) / QB)
+        return fail(ABSA_ERR_UNSUPPORTED, "B*H*ceil(N/128) must be below 2^31");
+    return ABSA_OK;
+}
+
+absa_status check_dtype(absa_dtype dt) {
+    if (dt != ABSA_BF16 && dt != ABSA_F32)
+        return fail(ABSA_ERR_UNSUPPORTED, "dtype must be ABSA_BF16 or ABSA_F32 (got %d)", (int)dt);
+    return ABSA_OK;
+}
+
+void fill_dims(absa_plan_s* p, int64_t B, int64_t H, int64_t N, int64_t d) {
+    p->B = B; p->H = H; p->N = N; p->d = d;
+    p->M = N / kKvBlock;
+    p->QB = (N + kQueryBlock - 1) / kQueryBlock;
+    p->rows = B * H * p->QB;
+}
+
+// SIP on device scores, shared by plan_create and plan_from_scores. Fills
+// rowptr/idx/logw/p of plan (allocated in arena). One device-to-host read of
+// the total count and the score check flag, then the fill kernel.
+absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_t seed,
+                    hipStream_t s, DeviceArena& arena) {
+    const int64_t rows = P->rows;
+    const int64_t words = (P->M + 63) / 64;
+    uint64_t* capmask = nullptr;
+    SipRow* rowinfo = nullptr;
+    int64_t* counts = nullptr;
+    PlanStatus* status = nullptr;
+    ABSA_TRY(arena.alloc(&capmask, rows * words, "cap mask"));
+    ABSA_TRY(arena.alloc(&rowinfo, rows, "row info"));
+    ABSA_TRY(arena.alloc(&counts, rows, "row counts"));
+    ABSA_TRY(arena.alloc(&status, 1, "plan status"));
+    ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
+    ABSA_HIP(hipMemsetAsync(status, 0, sizeof(PlanStatus), s), "clear plan status");
+    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed,
+                              reinterpret_cast<uint32_t*>(capmask), rowinfo, counts, status, s),
+             "SIP count kernel");
+    ABSA_HIP(launch_scan(counts, rows, P->rowptr, status, s), "row scan kernel");
+    PlanStatus host{};
+    ABSA_HIP(hipMemcpyAsync(&host, status, sizeof(PlanStatus), hipMemcpyDeviceToHost, s),
+             "read plan size");
+    ABSA_HIP(hipStreamSynchronize(s), "plan synchronisation");
+    if (host.bad_scores)
+        return fail(ABSA_ERR_INVALID_ARG,
+                    "scores must lie in [0, 1] and every row must sum to less than 2");
+    P->nnz = host.nnz;
+    ABSA_TRY(arena.alloc(&P->idx, P->nnz, "plan indices"));
+    ABSA_TRY(arena.alloc(&P->logw, P->nnz, "plan log-weights"));
+    ABSA_TRY(arena.alloc(&P->p, P->nnz, "plan probabilities"));
+    if (P->nnz > 0) {
+        ABSA_HIP(launch_sip_fill(scores, P->B, P->H, P->QB, P->M, seed,
+                                 reinterpret_cast<const uint32_t*>(capmask), rowinfo, P->rowptr,
+                                 P->idx, P->logw, P->p, s),
+                 "SIP fill kernel");
+    }
+    ABSA_HIP(hipStreamSynchronize(s), "plan completion");
+    return ABSA_OK;
+}
+
+void keep(DeviceArena& arena, absa_plan_s* P) {
+    arena.release(P->rowptr);
+    arena.release(P->idx);
+    arena.release(P->logw);
+    arena.release(P->p);
+    arena.release(P->kbar);
+    arena.release(P->cent);
+    arena.release(P->w);
+    arena.release(P->scores);
+}
+
+void free_plan(absa_plan_s* P) {
+    if (!P) return;
+    void* bufs[] = {P->rowptr, P->idx, P->logw, P->p, P->kbar, P->cent, P->w, P->scores};
+    for (void* b : bufs)
+        if (b) (void)hipFree(b);
+    delete P;
+}
+
+}  // namespace
+
+extern "C" {
+
+absa_status absa_plan_params_init(absa_plan_params* out) {
+    if (!out) return fail(ABSA_ERR_INVALID_ARG, "params is NULL");
+    out->query_block = kQueryBlock;
+    out->kv_block = kKvBlock;
+    out->n_clusters = 8;
+    out->kmeans_iters = 4;
+    out->budget_blocks = 1;
+    out->seed = 0;
+    out->keep_intermediates = 0;
+    out->reserved = 0;
+    return ABSA_OK;
+}
+
+absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int64_t B,
+                             int64_t H, int64_t N, int64_t d, const absa_plan_params* params,
+                             void* hip_stream, absa_plan* out) {
+    if (!out) return fail(ABSA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!q || !k || !params) return fail(ABSA_ERR_INVALID_ARG, "q, k and params must be non-NULL");
+    ABSA_TRY(check_dtype(dtype));
+    ABSA_TRY(check_shape(B, H, N, d));
+    if (params->query_block != kQueryBlock)
+        return fail(ABSA_ERR_UNSUPPORTED, "query_block must be 128 (got %d)", params->query_block);
+    if (params->kv_block != kKvBlock)
+        return fail(ABSA_ERR_UNSUPPORTED, "kv_block must be 4 (got %d)", params->kv_block);
+    if (params->n_clusters < 1 || params->n_clusters > kMaxClusters)
+        return fail(ABSA_ERR_UNSUPPORTED, "n_clusters must lie in [1, %d] (got %d)", kMaxClusters,
+                    params->n_clusters);
+    if (params->kmeans_iters < 1 || params->kmeans_iters > 64)
+        return fail(ABSA_ERR_INVALID_ARG, "kmeans_iters must lie in [1, 64] (got %d)",
+                    params->kmeans_iters);
+    if (params->reserved != 0) return fail(ABSA_ERR_INVALID_ARG, "params.reserved must be 0");
+    const int64_t M = N / kKvBlock;
+    if (params->budget_blocks < 1 || params->budget_blocks > M)
+        return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
+                    (long long)M, (long long)params->budget_blocks);
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    absa_plan_s* P = new (std::nothrow) absa_plan_s();
+    if (!P) return fail(ABSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+    fill_dims(P, B, H, N, d);
+    P->n_clusters = params->n_clusters;
+    const int C = params->n_clusters;
+    const Dtype dt = (dtype == ABSA_BF16) ? kBF16 : kF32;
+
+    absa_status st = [&]() -> absa_status {
+        DeviceArena arena;
+        ABSA_TRY(arena.alloc(&P->kbar, B * H * M * d, "mean keys"));
+        ABSA_TRY(arena.alloc(&P->cent, P->rows * C * d, "centroids"));
+        ABSA_TRY(arena.alloc(&P->w, P->rows * C, "cluster weights"));
+        ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), P->kbar, s),
+                 "mean-key kernel");
+        ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
+                               P->cent, P->w, s),
+                 "k-means kernel");
+        ABSA_HIP(launch_scores(P->cent, P->w, P->kbar, B * H, P->QB, M, static_cast<int>(d), C,
+                               P->scores, s),
+                 "score kernel");
+        ABSA_TRY(run_sip(P, P->scores, params->budget_blocks, params->seed, s, arena));
+        keep(arena, P);
+        if (!params->keep_intermediates) {
+            // the stream is idle after run_sip's final synchronisation
+            (void)hipFree(P->kbar); P->kbar = nullptr;
+            (void)hipFree(P->cent); P->cent = nullptr;
+            (void)hipFree(P->w); P->w = nullptr;
+            (void)hipFree(P->scores); P->scores = nullptr;
+        }
+        return ABSA_OK;
+    }();
+    if (st != ABSA_OK) {
+        P->rowptr = nullptr; P->idx = nullptr; P->logw = nullptr; P->p = nullptr;
+        P->kbar = P->cent = P->w = P->scores = nullptr;
+        delete P;
+        return st;
+    }
+    *out = P;
+    return ABSA_OK;
+}
+
+absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H, int64_t N,
+                                  int64_t d, int64_t budget_blocks, uint64_t seed,
+                                  void* hip_stream, absa_plan* out) {
+    if (!out) return fail(ABSA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!scores_dev) return fail(ABSA_ERR_INVALID_ARG, "scores is NULL");
+    ABSA_TRY(check_shape(B, H, N, d));
+    const int64_t M = N / kKvBlock;
+    if (budget_blocks < 1 || budget_blocks > M)
+        return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
+                    (long long)M, (long long)budget_blocks);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    absa_plan_s* P = new (std::nothrow) absa_plan_s();
+    if (!P) return fail(ABSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+    fill_dims(P, B, H, N, d);
+    absa_status st = [&]() -> absa_status {
+        DeviceArena arena;
+        ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, s, arena));
+        keep(arena, P);
+        return ABSA_OK;
+    }();
+    if (st != ABSA_OK) {
+        delete P;
+        return st;
+    }
+    *out = P;
+    return ABSA_OK;
+}
+
+absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx, const float* logw,
+                             const double* p, int64_t B, int64_t H, int64_t N, int64_t d,
+                             void* hip_stream, absa_plan* out) {
+    if (!out) return fail(ABSA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!rowptr) return fail(ABSA_ERR_INVALID_ARG, "rowptr is NULL");
+    ABSA_TRY(check_shape(B, H, N, d));
+    absa_plan_s tmp;
+    fill_dims(&tmp, B, H, N, d);
+    if (rowptr[0] != 0) return fail(ABSA_ERR_INVALID_ARG, "rowptr[0] must be 0");
+    for (int64_t i = 0; i < tmp.rows; ++i) {
+        const int64_t lo = rowptr[i], hi = rowptr[i + 1];
+        if (hi < lo) return fail(ABSA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)i);
+        if (hi - lo > tmp.M)
+            return fail(ABSA_ERR_INVALID_ARG, "row %lld holds more than M blocks", (long long)i);
+    }
+    const int64_t nnz = rowptr[tmp.rows];
+    if (nnz > 0 && (!idx || !logw))
+        return fail(ABSA_ERR_INVALID_ARG, "idx and logw must be non-NULL when the plan is not empty");
+    for (int64_t i = 0; i < tmp.rows; ++i) {
+        for (int64_t e = rowptr[i]; e < rowptr[i + 1]; ++e) {
+            if (idx[e] < 0 || idx[e] >= tmp.M)
+                return fail(ABSA_ERR_INVALID_ARG, "idx[%lld] = %d is outside [0, M)", (long long)e,
+                            idx[e]);
+            if (e > rowptr[i] && idx[e] <= idx[e - 1])
+                return fail(ABSA_ERR_INVALID_ARG, "indices of row %lld are not strictly ascending",
+                            (long long)i);
+            if (!std::isfinite(logw[e]))
+                return fail(ABSA_ERR_INVALID_ARG, "logw[%lld] is not finite", (long long)e);
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    absa_plan_s* P = new (std::nothrow) absa_plan_s();
+    if (!P) return fail(ABSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+    *P = tmp;
+    P->nnz = nnz;
+    absa_status st = [&]() -> absa_status {
+        DeviceArena arena;
+        ABSA_TRY(arena.alloc(&P->rowptr, P->rows + 1, "row pointers"));
+        ABSA_TRY(arena.alloc(&P->idx, nnz, "plan indices"));
+        ABSA_TRY(arena.alloc(&P->logw, nnz, "plan log-weights"));
+        ABSA_TRY(arena.alloc(&P->p, nnz, "plan probabilities"));
+        std::vector<double> pv;
+        const double* psrc = p;
+        if (!psrc && nnz > 0) {
+            pv.resize(static_cast<size_t>(nnz));
+            for (int64_t e = 0; e < nnz; ++e) pv[e] = std::exp(-static_cast<double>(logw[e]));
+            psrc = pv.data();
+        }
+        ABSA_HIP(hipMemcpyAsync(P->rowptr, rowptr, (P->rows + 1) * sizeof(int64_t),
+                                hipMemcpyHostToDevice, s), "copy row pointers");
+        if (nnz > 0) {
+            ABSA_HIP(hipMemcpyAsync(P->idx, idx, nnz * sizeof(int32_t), hipMemcpyHostToDevice, s),
+                     "copy indices");
+            ABSA_HIP(hipMemcpyAsync(P->logw, logw, nnz * sizeof(float), hipMemcpyHostToDevice, s),
+                     "copy log-weights");
+            ABSA_HIP(hipMemcpyAsync(P->p, psrc, nnz * sizeof(double), hipMemcpyHostToDevice, s),
+                     "copy probabilities");
+        }
+        ABSA_HIP(hipStreamSynchronize(s), "plan import");
+        keep(arena, P);
+        return ABSA_OK;
+    }();
+    if (st != ABSA_OK) {
+        delete P;
+        return st;
+    }
+    *out = P;
+    return ABSA_OK;
+}
+
+absa_status absa_plan_info(absa_plan plan, int64_t* shape4, int64_t* rows, int64_t* M,
+                           int64_t* nnz) {
+    if (!plan) return fail(ABSA_ERR_INVALID_ARG, "plan is NULL");
+    if (shape4) { shape4[0] = plan->B; shape4[1] = plan->H; shape4[2] = plan->N; shape4[3] = plan->d; }
+    if (rows) *rows = plan->rows;
+    if (M) *M = plan->M;
+    if (nnz) *nnz = plan->nnz;
+    return ABSA_OK;
+}
+
+absa_status absa_plan_export(absa_plan plan, int64_t* rowptr, int32_t* idx, float* logw,
+                             double* p) {
+    if (!plan) return fail(ABSA_ERR_INVALID_ARG, "plan is NULL");
+    if (rowptr)
+        ABSA_HIP(hipMemcpy(rowptr, plan->rowptr, (plan->rows + 1) * sizeof(int64_t),
+                           hipMemcpyDeviceToHost), "export row pointers");
+    if (plan->nnz > 0) {
+        if (idx)
+            ABSA_HIP(hipMemcpy(idx, plan->idx, plan->nnz * sizeof(int32_t), hipMemcpyDeviceToHost),
+                     "export indices");
+        if (logw)
+            ABSA_HIP(hipMemcpy(logw, plan->logw, plan->nnz * sizeof(float), hipMemcpyDeviceToHost),
+                     "export log-weights");
+        if (p)
+            ABSA_HIP(hipMemcpy(p, plan->p, plan->nnz * sizeof(double), hipMemcpyDeviceToHost),
+                     "export probabilities");
+    }
+    return ABSA_OK;
+}
+
+absa_status absa_plan_export_intermediate(absa_plan plan, absa_intermediate which, int64_t offset,
+                                          int64_t count, float* dst) {
+    if (!plan) return fail(ABSA_ERR_INVALID_ARG, "plan is NULL");
+    if (!dst && count > 0) return fail(ABSA_ERR_INVALID_ARG, "dst is NULL");
+    const float* src = nullptr;
+    int64_t total = 0;
+    switch (which) {
+        case ABSA_INTER_MEAN_KEYS: src = plan->kbar; total = plan->B * plan->H * plan->M * plan->d; break;
+        case ABSA_INTER_CENTROIDS: src = plan->cent; total = plan->rows * plan->n_clusters * plan->d; break;
+        case ABSA_INTER_WEIGHTS: src = plan->w; total = plan->rows * plan->n_clusters; break;
+        case ABSA_INTER_SCORES: src = plan->scores; total = plan->rows * plan->M; break;
+        default: return fail(ABSA_ERR_INVALID_ARG, "unknown intermediate %d", (int)which);
+    }
+    if (!src) return fail(ABSA_ERR_INVALID_ARG, "the plan did not keep its intermediates");
+    if (offset < 0 || count < 0 || offset > total || count > total - offset)
+        return fail(ABSA_ERR_INVALID_ARG, "range [%lld, +%lld) outside [0, %lld)", (long long)offset,
+                    (long long)count, (long long)total);
+    if (count > 0)
+        ABSA_HIP(hipMemcpy(dst, src + offset, count * sizeof(float), hipMemcpyDeviceToHost),
+                 "export intermediate");
+    return ABSA_OK;
+}
+
+static absa_status attention_common(const void* q, const void* k, const void* v, void* o,
+                                    absa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d) {
+    if (!q || !k || !v || !o) return fail(ABSA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+    ABSA_TRY(check_dtype(dtype));
+    return check_shape(B, H, N, d);
+}
+
+absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k, const void* v,
+                                  void* o, absa_dtype dtype, int64_t B, int64_t H, int64_t N,
+                                  int64_t d, void* hip_stream) {
+    if (!plan) return fail(ABSA_ERR_INVALID_ARG, "plan is NULL");
+    ABSA_TRY(attention_common(q, k, v, o, dtype, B, H, N, d));
+    if (plan->B != B || plan->H != H || plan->N != N || plan->d != d)
+        return fail(ABSA_ERR_PLAN_MISMATCH,
+                    "plan built for (B,H,N,d) = (%lld,%lld,%lld,%lld), called with (%lld,%lld,%lld,%lld)",
+                    (long long)plan->B, (long long)plan->H, (long long)plan->N, (long long)plan->d,
+                    (long long)B, (long long)H, (long long)N, (long long)d);
+    ABSA_HIP(launch_attention(q, k, v, o, dtype == ABSA_BF16 ? kBF16 : kF32, B, H, N,
+                              static_cast<int>(d), plan->rowptr, plan->idx, plan->logw, false,
+                              static_cast<hipStream_t>(hip_stream)),
+             "sparse attention kernel");
+    return ABSA_OK;
+}
+
+absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
+                                 absa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 void* hip_stream) {
+    ABSA_TRY(attention_common(q, k, v, o, dtype, B, H, N, d));
+    ABSA_HIP(launch_attention(q, k, v, o, dtype == ABSA_BF16 ? kBF16 : kF32, B, H, N,
+                              static_cast<int>(d), nullptr, nullptr, nullptr, true,
+                              static_cast<hipStream_t>(hip_stream)),
+             "dense attention kernel");
+    return ABSA_OK;
+}
+
+void absa_plan_destroy(absa_plan plan) {
+    if (!plan) return;
+    free_plan(plan);
+}
+
+const char* absa_status_string(absa_status status) {
+    switch (status) {
+        case ABSA_OK: return "ABSA_OK";
+        case ABSA_ERR_INVALID_ARG: return "ABSA_ERR_INVALID_ARG";
+        case ABSA_ERR_UNSUPPORTED: return "ABSA_ERR_UNSUPPORTED";
+        case ABSA_ERR_OUT_OF_MEMORY: return "ABSA_ERR_OUT_OF_MEMORY";
+        case ABSA_ERR_DEVICE: return "ABSA_ERR_DEVICE";
+        case ABSA_ERR_PLAN_MISMATCH: return "ABSA_ERR_PLAN_MISMATCH";
+    }
+    return "ABSA_UNKNOWN_STATUS";
+}
+
+const char* absa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

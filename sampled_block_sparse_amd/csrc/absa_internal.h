@@ -1,0 +1,64 @@
+// Internal declarations shared by the host layer (absa.cpp) and the HIP
+// kernel sources. Not part of the public interface (include/absa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace absa {
+
+constexpr int kQueryBlock = 128;   // queries per plan row
+constexpr int kKvBlock = 4;        // tokens per KV block
+constexpr int kMaxClusters = 16;
+
+enum Dtype : int { kBF16 = 0, kF32 = 1 };
+
+// Per-row outcome of the capped water-filling, written by the SIP count
+// kernel and read by the fill kernel.
+//   mode 0: every still-active block has p = 1
+//   mode 1: every still-active block has p = left / n_active (all scores 0)
+//   mode 2: every still-active block has p = c * q_j
+// Blocks capped in an earlier round carry a set bit in the row's cap mask.
+struct SipRow {
+    double c;          // mode 2 multiplier, or left/n_active for mode 1
+    int32_t mode;
+    int32_t pad;
+};
+
+// Device-side status written at the end of the SIP count + scan and read
+// back by the host in the plan's single synchronisation.
+struct PlanStatus {
+    int64_t nnz;
+    int32_t bad_scores;   // a score outside [0,1] / NaN, or a row sum >= 2
+    int32_t pad;
+};
+
+hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
+                            float* kbar, hipStream_t s);
+
+hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
+                         int C, int iters, float* cent, float* w, hipStream_t s);
+
+hipError_t launch_scores(const float* cent, const float* w, const float* kbar,
+                         int64_t BH, int64_t QB, int64_t M, int d, int C,
+                         float* scores, hipStream_t s);
+
+hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
+                            int64_t M, int64_t budget, uint64_t seed,
+                            uint32_t* capmask, SipRow* rowinfo, int64_t* counts,
+                            PlanStatus* status, hipStream_t s);
+
+hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr,
+                       PlanStatus* status, hipStream_t s);
+
+hipError_t launch_sip_fill(const float* scores, int64_t B, int64_t H, int64_t QB,
+                           int64_t M, uint64_t seed, const uint32_t* capmask,
+                           const SipRow* rowinfo, const int64_t* rowptr,
+                           int32_t* idx, float* logw, double* p, hipStream_t s);
+
+hipError_t launch_attention(const void* q, const void* k, const void* v, void* o,
+                            Dtype dt, int64_t B, int64_t H, int64_t N, int d,
+                            const int64_t* rowptr, const int32_t* idx,
+                            const float* logw, bool dense, hipStream_t s);
+
+}  // namespace absa

@@ -1,0 +1,653 @@
+// Plan kernels for AB-Attention on gfx950: mean keys, IBCS k-means, IBCS
+// scores, SIP probabilities / draws / CSR.
+//
+// Method sources (web pages):
+//   [hamidun] "AB-Attention speeds up video generation up to 2.23x and skips
+//             92% of attention compute", section "three techniques in
+//             AB-Attention", IBCS and SIP paragraphs.
+//   [edumints] "AB-Attention: ... Dogru Blok Dikkat Mekanizmasi", section
+//             "three innovations".
+#include "absa_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace absa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) {
+    return bf16_to_f32(*p);
+}
+
+// ---------------------------------------------------------------------------
+// Mean keys [hamidun, IBCS paragraph: "averaged keys"]:
+// kbar[bh, j, :] = (k[bh, 4j] + k[bh, 4j+1] + k[bh, 4j+2] + k[bh, 4j+3]) / 4.
+// One thread per (bh, j, 4-channel chunk); the fp32 sum of four bf16 values
+// is exact unless their exponents differ by more than 15.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kbar,
+                                 int64_t chunks, int d) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (c >= chunks) return;
+    const int per_row = d >> 2;
+    const int64_t blk = c / per_row;            // flattened bh*M + j
+    const int d0 = static_cast<int>(c - blk * per_row) << 2;
+    const T* src = k + (blk * kKvBlock) * d + d0;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kKvBlock; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += load_f32(src + t * d + e);
+    }
+    float4 out = make_float4(acc[0] * 0.25f, acc[1] * 0.25f, acc[2] * 0.25f, acc[3] * 0.25f);
+    *reinterpret_cast<float4*>(kbar + blk * d + d0) = out;
+}
+
+// ---------------------------------------------------------------------------
+// IBCS k-means [hamidun, IBCS paragraph; edumints, IBCS item]: one workgroup
+// per query block. Lloyd iterations in fp64 on the block's queries in their
+// original order; initial centroids are the queries floor(m*n/C_eff);
+// nearest centroid by squared distance, ties to the smaller index; a cluster
+// left empty keeps its centroid. Outputs fp32 centroids [row, C, d] and
+// weights [row, C] = member share of the block's n queries under the last
+// assignment (C_eff = min(C, n); further clusters are zero with weight 0).
+// The centroid sums of bf16/fp32 inputs are exact in fp64, so each centroid
+// is the correctly rounded mean whatever the summation order.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, int64_t N,
+                                                     int64_t QB, int d, int C, int iters,
+                                                     float* __restrict__ cent_out,
+                                                     float* __restrict__ w_out) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int qstride = d + 1;                    // odd stride: conflict-free columns
+    float* qs = reinterpret_cast<float*>(smem);                                   // [128][d+1]
+    double* cs = reinterpret_cast<double*>(smem + ((kQueryBlock * qstride * 4 + 15) & ~15));  // [C][d]
+    __shared__ double bdist[2][kQueryBlock];
+    __shared__ int bidx[2][kQueryBlock];
+    __shared__ int assign[kQueryBlock];
+    __shared__ int counts[kMaxClusters];
+
+    const int64_t row = blockIdx.x;
+    const int64_t bh = row / QB;
+    const int64_t r = row - bh * QB;
+    const int64_t lo = r * kQueryBlock;
+    const int n = static_cast<int>(min<int64_t>(kQueryBlock, N - lo));
+    const int ceff = min(C, n);
+    const int tid = threadIdx.x;
+    const T* qrow = q + (bh * N + lo) * d;
+
+    for (int e = tid; e < n * d; e += blockDim.x) {
+        const int i = e / d, dd = e - i * d;
+        qs[i * qstride + dd] = load_f32(qrow + e);
+    }
+    __syncthreads();
+    for (int e = tid; e < ceff * d; e += blockDim.x) {
+        const int m = e / d, dd = e - m * d;
+        cs[e] = static_cast<double>(qs[((m * n) / ceff) * qstride + dd]);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < iters; ++it) {
+        // Assignment: thread (i, half) scans clusters half, half+2, ...
+        {
+            const int i = tid & (kQueryBlock - 1);
+            const int half = tid >> 7;
+            if (i < n) {
+                double best = 0.0;
+                int bm = -1;
+                for (int m = half; m < ceff; m += 2) {
+                    double dist = 0.0;
+                    const float* qi = qs + i * qstride;
+                    const double* cm = cs + m * d;
+                    for (int dd = 0; dd < d; ++dd) {
+                        const double df = static_cast<double>(qi[dd]) - cm[dd];
+                        dist = fma(df, df, dist);
+                    }
+                    if (bm < 0 || dist < best) { best = dist; bm = m; }
+                }
+                bdist[half][i] = best;
+                bidx[half][i] = bm;
+            }
+        }
+        __syncthreads();
+        if (tid < n) {
+            int a = bidx[0][tid];
+            const int m1 = bidx[1][tid];
+            if (m1 >= 0) {
+                const double d0 = bdist[0][tid], d1 = bdist[1][tid];
+                if (d1 < d0 || (d1 == d0 && m1 < a)) a = m1;
+            }
+            assign[tid] = a;
+        }
+        __syncthreads();
+        if (tid < ceff) {
+            int cnt = 0;
+            for (int i = 0; i < n; ++i) cnt += (assign[i] == tid);
+            counts[tid] = cnt;
+        }
+        // Update: each (cluster, channel) pair owned by one thread.
+        for (int e = tid; e < ceff * d; e += blockDim.x) {
+            const int m = e / d, dd = e - m * d;
+            double s = 0.0;
+            int cnt = 0;
+            for (int i = 0; i < n; ++i) {
+                if (assign[i] == m) { s += static_cast<double>(qs[i * qstride + dd]); ++cnt; }
+            }
+            if (cnt) cs[e] = s / static_cast<double>(cnt);
+        }
+        __syncthreads();
+    }
+
+    float* co = cent_out + row * C * d;
+    for (int e = tid; e < C * d; e += blockDim.x) {
+        const int m = e / d;
+        co[e] = (m < ceff) ? static_cast<float>(cs[e]) : 0.0f;
+    }
+    if (tid < C) {
+        w_out[row * C + tid] = (tid < ceff)
+            ? static_cast<float>(static_cast<double>(counts[tid]) / static_cast<double>(n))
+            : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// IBCS scores [hamidun, IBCS paragraph]: for each query block r and KV block
+// j, s_j = sum_m w_m * softmax_j(c_m . kbar_j / sqrt(d)), softmax over all M
+// KV blocks of the head. This is a dense fp32 contraction
+// (centroids x mean keys, per head) and runs on fp32 MFMA 32x32x2:
+// a wave owns 32 centroid slots (32/CP query blocks of CP slots; slots past C
+// have weight 0) against 32-key tiles staged in LDS. Pass 1 keeps per-lane
+// running (max, sum) of each centroid's exponentials and merges them across
+// lanes; pass 2 recomputes the logits and writes the weighted sum over the
+// block's clusters. MFMA D layout (32x32): lane l holds column l%32 and rows
+// (i/4)*8 + (l/32)*4 + i%4 for i < 16.
+// ---------------------------------------------------------------------------
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreTile = 32;
+
+template <int CP, int D>
+__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ cent,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ kbar,
+                                                     int64_t QB, int64_t M, int C,
+                                                     float scale_log2,
+                                                     float* __restrict__ scores) {
+    constexpr int RPW = 32 / CP;                    // query blocks per wave
+    constexpr int KS = D + 2;                       // LDS row stride (floats)
+    __shared__ __align__(16) float ks[kScoreTile * KS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t bh = blockIdx.y;
+    const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * kScoreWaves + wave) * RPW;
+
+    // A operand: this lane's centroid slot (row col of the 32x32 block).
+    const int64_t my_r = r0 + col / CP;
+    const int my_m = col % CP;
+    const bool slot_ok = (my_r < QB) && (my_m < C);
+    float a[D / 2];
+    {
+        const float* src = cent + ((bh * QB + my_r) * C + my_m) * D;
+#pragma unroll
+        for (int s = 0; s < D / 2; ++s) a[s] = slot_ok ? src[2 * s + half] : 0.0f;
+    }
+
+    const float* kb = kbar + bh * M * D;
+    const int64_t ntiles = (M + kScoreTile - 1) / kScoreTile;
+
+    auto load_tile = [&](int64_t t) {
+        const int64_t j0 = t * kScoreTile;
+        for (int e = tid * 4; e < kScoreTile * D; e += 256 * 4) {
+            const int key = e / D, dd = e - key * D;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + key < M) v = *reinterpret_cast<const float4*>(kb + (j0 + key) * D + dd);
+            float* dst = ks + key * KS + dd;
+            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+        }
+    };
+    auto tile_logits = [&]() {
+        floatx16 acc = {};
+#pragma unroll
+        for (int s = 0; s < D / 2; ++s) {
+            const float b = ks[col * KS + 2 * s + half];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b, acc, 0, 0, 0);
+        }
+        return acc;
+    };
+
+    // Pass 1: running max and sum per centroid row held by this lane.
+    float mx[16], zs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { mx[i] = -INFINITY; zs[i] = 0.0f; }
+    for (int64_t t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        load_tile(t);
+        __syncthreads();
+        const floatx16 acc = tile_logits();
+        if (t * kScoreTile + col < M) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float x = acc[i] * scale_log2;
+                const float mn = fmaxf(mx[i], x);
+                zs[i] = zs[i] * exp2f(mx[i] - mn) + exp2f(x - mn);
+                mx[i] = mn;
+            }
+        }
+    }
+    // Merge the 32 columns of each half (xor over lane bits 0..4).
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float m2 = __shfl_xor(mx[i], off);
+            const float z2 = __shfl_xor(zs[i], off);
+            const float mn = fmaxf(mx[i], m2);
+            const float e1 = (mx[i] == -INFINITY) ? 0.0f : zs[i] * exp2f(mx[i] - mn);
+            const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * exp2f(m2 - mn);
+            zs[i] = e1 + e2;
+            mx[i] = mn;
+        }
+    }
+    // Coefficient w_m / Z_m of every row this lane holds.
+    float coef[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int slot = (i >> 2) * 8 + half * 4 + (i & 3);
+        const int64_t rr = r0 + slot / CP;
+        const int mm = slot % CP;
+        const bool ok = (rr < QB) && (mm < C);
+        coef[i] = ok ? w[(bh * QB + rr) * C + mm] / zs[i] : 0.0f;
+        if (!ok) mx[i] = 0.0f;
+    }
+
+    // Pass 2: weighted sum over each query block's clusters.
+    for (int64_t t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        load_tile(t);
+        __syncthreads();
+        const floatx16 acc = tile_logits();
+        float part[RPW];
+#pragma unroll
+        for (int g = 0; g < RPW; ++g) part[g] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int slot = (i >> 2) * 8 + half * 4 + (i & 3);
+            const float e = exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
+            part[slot / CP] += e;
+        }
+        const int64_t j = t * kScoreTile + col;
+        if (CP >= 8) {
+            // A query block's clusters span both halves: add the partner's.
+#pragma unroll
+            for (int g = 0; g < RPW; ++g) part[g] += __shfl_xor(part[g], 32);
+#pragma unroll
+            for (int g = 0; g < RPW; ++g) {
+                const int64_t rr = r0 + g;
+                if ((g & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = part[g];
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < RPW; ++g) {
+                // rows g with bit (CP's half bit) matching this half
+                const int half_of_g = ((g * CP) >> 2) & 1;
+                const int64_t rr = r0 + g;
+                if (half_of_g == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = part[g];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide reductions (256 threads = 4 waves).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
+    v = wave_sum_u64(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    uint64_t t = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) t += red[i];
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): 4-word counter, 2-word
+// key; 10 rounds of two 32x32->64 multiplies with the Weyl key schedule.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+    constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
+        const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0;
+        const uint32_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+        k0 += W0; k1 += W1;
+    }
+}
+
+// Uniform in [0, 1) for KV block j of row (b, h, r): 53 high bits of the
+// first two output words.
+__device__ __forceinline__ double sip_uniform(uint64_t seed, int64_t b, int64_t h, int64_t r,
+                                              int64_t j) {
+    uint32_t c[4] = {static_cast<uint32_t>(j), static_cast<uint32_t>(r),
+                     static_cast<uint32_t>(h), static_cast<uint32_t>(b)};
+    philox_10(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+    const uint64_t u53 = ((static_cast<uint64_t>(c[0]) << 32) | c[1]) >> 11;
+    return static_cast<double>(u53) * 0x1.0p-53;
+}
+
+__device__ __forceinline__ uint64_t fixed_point(float s) {
+    return static_cast<uint64_t>(floor(static_cast<double>(s) * 0x1.0p52));
+}
+
+// p of block j given the row's outcome. capped blocks have p = 1.
+__device__ __forceinline__ double sip_p(bool capped, const SipRow& ri, uint64_t q) {
+    if (capped || ri.mode == 0) return 1.0;
+    if (ri.mode == 1) return ri.c;
+    return ri.c * static_cast<double>(q);
+}
+
+// ---------------------------------------------------------------------------
+// SIP probabilities and draw count [hamidun, SIP paragraph; edumints, SIP
+// item]: capped water-filling in exact fixed point (q_j = floor(s_j 2^52),
+// integer sums, IEEE double division and product), then one Poisson draw per
+// block. One workgroup per plan row. The cap mask (one bit per block) and the
+// final multiplier go to global memory for the fill kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sip_count_kernel(
+    const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
+    uint64_t seed, uint64_t* __restrict__ capmask, SipRow* __restrict__ rowinfo,
+    int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    __shared__ uint64_t red[4];
+    const int64_t row = blockIdx.x;
+    const float* s = scores + row * M;
+    const int64_t words = (M + 63) / 64;
+    uint64_t* cm = capmask + row * words;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+
+    uint64_t sum = 0, bad = 0;
+    for (int64_t j = tid; j < M; j += 256) {
+        const float v = s[j];
+        if (!(v >= 0.0f && v <= 1.0f)) bad = 1;
+        else sum += fixed_point(v);
+    }
+    // each 64-block word is owned by the wave that later tests and sets it
+    for (int64_t base = 0; base < M; base += 256)
+        if (lane == 0 && base + tid < M) cm[(base + tid) >> 6] = 0;
+    const uint64_t total = block_sum_u64(sum, red);
+    const uint64_t nbad = block_sum_u64(bad, red);
+    if (nbad != 0 || total >= (1ull << 53)) {
+        if (tid == 0) {
+            status->bad_scores = 1;
+            counts[row] = 0;
+            rowinfo[row].mode = 0;
+            rowinfo[row].c = 0.0;
+        }
+        return;
+    }
+
+    int64_t taken = 0, n_active = M;
+    uint64_t S = total;
+    SipRow ri;
+    ri.pad = 0;
+    for (;;) {
+        const int64_t left = budget - taken;
+        if (left >= n_active) { ri.mode = 0; ri.c = 1.0; break; }
+        if (S == 0) {
+            ri.mode = 1;
+            ri.c = static_cast<double>(left) / static_cast<double>(n_active);
+            break;
+        }
+        const double c = static_cast<double>(left) / static_cast<double>(S);
+        uint64_t ncap = 0, scap = 0;
+        for (int64_t base = 0; base < M; base += 256) {
+            const int64_t j = base + tid;
+            bool hit = false;
+            uint64_t q = 0;
+            if (j < M) {
+                const bool was = (cm[j >> 6] >> (j & 63)) & 1ull;
+                q = fixed_point(s[j]);
+                hit = !was && (c * static_cast<double>(q) >= 1.0);
+            }
+            const uint64_t ballot = __ballot(hit);
+            if (hit) { ++ncap; scap += q; }
+            if (lane == 0 && ballot) cm[j >> 6] |= ballot;
+        }
+        const uint64_t tcap = block_sum_u64(ncap, red);
+        const uint64_t tsum = block_sum_u64(scap, red);
+        if (tcap == 0) { ri.mode = 2; ri.c = c; break; }
+        taken += static_cast<int64_t>(tcap);
+        n_active -= static_cast<int64_t>(tcap);
+        S -= tsum;
+    }
+
+    const int64_t bidx = row / QB;
+    const int64_t r = row - bidx * QB;
+    const int64_t h = bidx % H;
+    const int64_t b = bidx / H;
+    uint64_t kept = 0;
+    for (int64_t j = tid; j < M; j += 256) {
+        const bool capped = (cm[j >> 6] >> (j & 63)) & 1ull;
+        const double p = sip_p(capped, ri, fixed_point(s[j]));
+        kept += (sip_uniform(seed, b, h, r, j) < p) ? 1 : 0;
+    }
+    const uint64_t tk = block_sum_u64(kept, red);
+    if (tid == 0) {
+        counts[row] = static_cast<int64_t>(tk);
+        rowinfo[row] = ri;
+    }
+}
+
+// Exclusive scan of the per-row counts into rowptr[0..rows]; one workgroup.
+__global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ counts,
+                                                    int64_t rows, int64_t* __restrict__ rowptr,
+                                                    PlanStatus* __restrict__ status) {
+    __shared__ int64_t wsum[16];
+    __shared__ int64_t carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < rows; base += 1024) {
+        const int64_t i = base + tid;
+        const int64_t v = (i < rows) ? counts[i] : 0;
+        int64_t incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int64_t woff = 0;
+        for (int k = 0; k < wave; ++k) woff += wsum[k];
+        const int64_t carry = carry_s;
+        if (i < rows) rowptr[i] = carry + woff + incl - v;
+        __syncthreads();
+        if (tid == 1023) carry_s = carry + woff + incl;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        rowptr[rows] = carry_s;
+        status->nnz = carry_s;
+    }
+}
+
+// Fill the CSR row: ascending kept block indices, fp32 log-weights -ln p
+// (+0 for p = 1), and p. Order-preserving compaction with wave ballots.
+__global__ __launch_bounds__(256) void sip_fill_kernel(
+    const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, uint64_t seed,
+    const uint64_t* __restrict__ capmask, const SipRow* __restrict__ rowinfo,
+    const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
+    double* __restrict__ p_out) {
+    __shared__ int64_t wcount[4];
+    const int64_t row = blockIdx.x;
+    const float* s = scores + row * M;
+    const int64_t words = (M + 63) / 64;
+    const uint64_t* cm = capmask + row * words;
+    const SipRow ri = rowinfo[row];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bidx = row / QB;
+    const int64_t r = row - bidx * QB;
+    const int64_t h = bidx % H;
+    const int64_t b = bidx / H;
+    int64_t pos = rowptr[row];
+    for (int64_t base = 0; base < M; base += 256) {
+        const int64_t j = base + tid;
+        bool keep = false;
+        double p = 0.0;
+        if (j < M) {
+            const bool capped = (cm[j >> 6] >> (j & 63)) & 1ull;
+            p = sip_p(capped, ri, fixed_point(s[j]));
+            keep = sip_uniform(seed, b, h, r, j) < p;
+        }
+        const uint64_t ballot = __ballot(keep);
+        const int before = __popcll(ballot & ((1ull << lane) - 1ull));
+        if (lane == 0) wcount[wave] = __popcll(ballot);
+        __syncthreads();
+        int64_t woff = 0, tot = 0;
+        for (int k = 0; k < 4; ++k) {
+            if (k < wave) woff += wcount[k];
+            tot += wcount[k];
+        }
+        if (keep) {
+            const int64_t at = pos + woff + before;
+            idx[at] = static_cast<int32_t>(j);
+            logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
+            p_out[at] = p;
+        }
+        pos += tot;
+        __syncthreads();
+    }
+}
+
+template <typename F>
+hipError_t launch_checked(F&& f) {
+    f();
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
+                            float* kbar, hipStream_t s) {
+    const int64_t chunks = BH * (N / kKvBlock) * (d / 4);
+    const int threads = 256;
+    const int64_t blocks = (chunks + threads - 1) / threads;
+    if (blocks == 0) return hipSuccess;
+    return launch_checked([&] {
+        if (dt == kBF16)
+            hipLaunchKernelGGL(mean_keys_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, s,
+                               static_cast<const uint16_t*>(k), kbar, chunks, d);
+        else
+            hipLaunchKernelGGL(mean_keys_kernel<float>, dim3(blocks), dim3(threads), 0, s,
+                               static_cast<const float*>(k), kbar, chunks, d);
+    });
+}
+
+hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d, int C,
+                         int iters, float* cent, float* w, hipStream_t s) {
+    const int64_t QB = (N + kQueryBlock - 1) / kQueryBlock;
+    const size_t qbytes = (static_cast<size_t>(kQueryBlock) * (d + 1) * 4 + 15) & ~size_t(15);
+    const size_t shm = qbytes + static_cast<size_t>(C) * d * 8;
+    // up to 82 KB of dynamic LDS at d = 128 (gfx950 has 160 KB per CU)
+    hipError_t e = (dt == kBF16)
+        ? hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_kernel<uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm))
+        : hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_kernel<float>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
+    if (e != hipSuccess) return e;
+    return launch_checked([&] {
+        if (dt == kBF16)
+            hipLaunchKernelGGL(kmeans_kernel<uint16_t>, dim3(BH * QB), dim3(256), shm, s,
+                               static_cast<const uint16_t*>(q), N, QB, d, C, iters, cent, w);
+        else
+            hipLaunchKernelGGL(kmeans_kernel<float>, dim3(BH * QB), dim3(256), shm, s,
+                               static_cast<const float*>(q), N, QB, d, C, iters, cent, w);
+    });
+}
+
+template <int CP>
+static void launch_scores_cp(const float* cent, const float* w, const float* kbar, int64_t BH,
+                             int64_t QB, int64_t M, int d, int C, float* scores,
+                             hipStream_t s) {
+    constexpr int rows_per_wg = kScoreWaves * (32 / CP);
+    const dim3 grid(static_cast<unsigned>((QB + rows_per_wg - 1) / rows_per_wg),
+                    static_cast<unsigned>(BH));
+    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(d));
+    if (d == 128)
+        hipLaunchKernelGGL((scores_kernel<CP, 128>), grid, dim3(256), 0, s, cent, w, kbar, QB, M,
+                           C, scale_log2, scores);
+    else
+        hipLaunchKernelGGL((scores_kernel<CP, 64>), grid, dim3(256), 0, s, cent, w, kbar, QB, M,
+                           C, scale_log2, scores);
+}
+
+hipError_t launch_scores(const float* cent, const float* w, const float* kbar, int64_t BH,
+                         int64_t QB, int64_t M, int d, int C, float* scores, hipStream_t s) {
+    return launch_checked([&] {
+        if (C <= 1) launch_scores_cp<1>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+        else launch_scores_cp<16>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+    });
+}
+
+hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
+                            int64_t budget, uint64_t seed, uint32_t* capmask, SipRow* rowinfo,
+                            int64_t* counts, PlanStatus* status, hipStream_t s) {
+    (void)B;
+    const int64_t rows = B * H * QB;
+    return launch_checked([&] {
+        hipLaunchKernelGGL(sip_count_kernel, dim3(rows), dim3(256), 0, s, scores, H, QB, M,
+                           budget, seed, reinterpret_cast<uint64_t*>(capmask), rowinfo, counts,
+                           status);
+    });
+}
+
+hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr, PlanStatus* status,
+                       hipStream_t s) {
+    return launch_checked([&] {
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, rows, rowptr, status);
+    });
+}
+
+hipError_t launch_sip_fill(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
+                           uint64_t seed, const uint32_t* capmask, const SipRow* rowinfo,
+                           const int64_t* rowptr, int32_t* idx, float* logw, double* p,
+                           hipStream_t s) {
+    const int64_t rows = B * H * QB;
+    return launch_checked([&] {
+        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, H, QB, M, seed,
+                           reinterpret_cast<const uint64_t*>(capmask), rowinfo, rowptr, idx,
+                           logw, p);
+    });
+}
+
+}  // namespace absa

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on
+inputs small enough for the oracle to finish in seconds while still spanning
+several tiles, partial query blocks and ragged key tiles."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sampled_block_sparse_amd as absa
+import synth
+from tests.gpu_util import (SCORE_REL, check_output, check_plan_exact, flips_explained,
+                            oracle_plan_of, score_error, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _inputs(name=None, B=None, H=None, N=None, d=None, dtype="bf16", seed=0):
+    if name is not None:
+        q, k, v = synth.make_inputs(name)
+    else:
+        q, k, v = (torch.from_numpy(x) for x in synth.iid_qkv(B, H, N, d, seed))
+        if dtype == "bf16":
+            q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    return q, k, v
+
+
+CASES = {
+    # name: (inputs kwargs, budget in blocks or pct)
+    "tiny25": (dict(name="tiny"), ("pct", 25)),
+    "small10": (dict(name="small"), ("pct", 10)),
+    "ragged_d128": (dict(B=2, H=3, N=1000, d=128, seed=5), ("pct", 10)),
+    "ragged_d64_f32": (dict(B=1, H=2, N=1340, d=64, dtype="f32", seed=6), ("pct", 20)),
+    "short_rows": (dict(B=1, H=2, N=200, d=128, seed=7), ("blocks", 3)),
+}
+
+
+def _budget(spec, M):
+    kind, val = spec
+    return synth.budget_blocks(val, M) if kind == "pct" else val
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    name = request.param
+    kw, bspec = CASES[name]
+    q, k, v = _inputs(**kw)
+    B, H, N, d = q.shape
+    M = N // 4
+    budget = _budget(bspec, M)
+    Q, K, V = to64(q), to64(k), to64(v)
+    scores, cents, wts = oracle.ibcs_scores(Q, K)
+    print(f"[case {name}] B={B} H={H} N={N} d={d} dtype={q.dtype} budget={budget}", flush=True)
+    return dict(name=name, q=q.to(DEV), k=k.to(DEV), v=v.to(DEV), Q=Q, K=K, V=V, B=B, H=H, N=N,
+                d=d, M=M, budget=budget, scores=scores, cents=cents, wts=wts)
+
+
+def test_dense_vs_oracle(case):
+    c = case
+    out = absa.absa_dense_attention(c["q"], c["k"], c["v"])
+    torch.cuda.synchronize()
+    if c["N"] > 4096:      # dense fp64 over every row is slow: check a sample of heads
+        hs = [0, c["H"] - 1]
+        ref = oracle.dense_attention(c["Q"][:, hs], c["K"][:, hs], c["V"][:, hs])
+        check_output(to64(out)[:, hs], ref, "dense")
+    else:
+        check_output(to64(out), oracle.dense_attention(c["Q"], c["K"], c["V"]), "dense")
+
+
+def test_plan_from_oracle_scores_is_bit_exact(case):
+    c = case
+    seed = synth.sip_seed(0)
+    s32 = c["scores"].astype(np.float32)
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), c["N"], c["d"], c["budget"],
+                                      seed)
+    ref = oracle.plan_from_scores(s32, c["B"], c["H"], c["N"], c["d"], c["budget"], seed)
+    n1 = check_plan_exact(plan.export(), ref, c["name"])
+    print(f"logw entries 1 ulp apart: {n1} of {ref.idx.size}")
+
+
+def test_sparse_with_imported_oracle_plan(case):
+    c = case
+    seed = synth.sip_seed(1)
+    ref_plan = oracle.plan_from_scores(c["scores"].astype(np.float32), c["B"], c["H"], c["N"],
+                                       c["d"], c["budget"], seed)
+    plan = absa.absa_plan_import(ref_plan.rowptr, ref_plan.idx, ref_plan.logw, ref_plan.p,
+                                 c["B"], c["H"], c["N"], c["d"])
+    out = absa.absa_sparse_attention(plan, c["q"], c["k"], c["v"])
+    torch.cuda.synchronize()
+    ref = oracle.plan_attention(c["Q"], c["K"], c["V"], ref_plan)
+    check_output(to64(out), ref, "sparse (imported plan)")
+
+
+def test_plan_create_stages_and_output(case):
+    c = case
+    B, H, N, d, M = c["B"], c["H"], c["N"], c["d"], c["M"]
+    QB = (N + 127) // 128
+    seed = synth.sip_seed(2)
+    plan = absa.absa_plan_create(c["q"], c["k"], c["budget"], seed, keep_intermediates=True)
+    # mean keys
+    kbar = plan.export_intermediate(absa.INTER_MEAN_KEYS).reshape(B, H, M, d)
+    ref_kbar = oracle.mean_keys(c["K"])
+    assert np.abs(kbar - ref_kbar).max() <= 2.0 ** -22 * max(1.0, np.abs(c["K"]).max())
+    # cluster weights (exact) and centroids (fp32 rounding of the fp64 means)
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8).reshape(B * H * QB, 8)
+    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * 8 * d).reshape(
+        B * H * QB, 8, d)
+    ref_w = c["wts"].reshape(-1, 8).astype(np.float32)
+    bad = np.nonzero((w != ref_w).any(axis=1))[0]
+    assert flips_explained(c["Q"], bad, N, 8, 4), f"weights differ in rows {bad[:10]}"
+    good = np.setdiff1d(np.arange(B * H * QB), bad)
+    ref_c = c["cents"].reshape(-1, 8, d)
+    assert np.abs(cen[good] - ref_c[good]).max() <= 1e-6 * max(1.0, np.abs(ref_c).max())
+    # scores within the stated relative tolerance
+    s = plan.export_intermediate(absa.INTER_SCORES).reshape(B * H * QB, M)
+    err = score_error(s[good], c["scores"].reshape(-1, M)[good])
+    print(f"score error max {err.max():.3e}; rows with assignment near-ties: {len(bad)}")
+    assert err.max() <= SCORE_REL
+    # the plan is the SIP rule applied to the GPU's own fp32 scores
+    gp = plan.export()
+    ref_plan = oracle.plan_from_scores(s.reshape(B, H, QB, M), B, H, N, d, c["budget"], seed)
+    check_plan_exact(gp, ref_plan, "plan_create")
+    # the output given that plan
+    out = absa.absa_sparse_attention(plan, c["q"], c["k"], c["v"])
+    torch.cuda.synchronize()
+    ref = oracle.plan_attention(c["Q"], c["K"], c["V"], oracle_plan_of(gp, B, H, N, d))
+    check_output(to64(out), ref, "sparse (own plan)")
+
+
+def test_full_budget_equals_dense():
+    q, k, v = (x.to(DEV) for x in synth.make_inputs("tiny"))
+    B, H, N, d = q.shape
+    plan = absa.absa_plan_create(q, k, N // 4, synth.sip_seed(0))
+    gp = plan.export()
+    assert (gp["p"] == 1).all() and (gp["logw"] == 0).all()
+    np.testing.assert_array_equal(np.diff(gp["rowptr"]), N // 4)
+    sparse = absa.absa_sparse_attention(plan, q, k, v)
+    dense = absa.absa_dense_attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse, dense)
+    check_output(to64(sparse), oracle.dense_attention(to64(q), to64(k), to64(v)), "budget 100%")
+
+
+@pytest.mark.parametrize("C,T", [(1, 4), (4, 2), (16, 4), (8, 1)])
+def test_cluster_and_iteration_variants(C, T):
+    q, k, v = _inputs(B=1, H=2, N=1000, d=64, seed=11)
+    Q, K = to64(q), to64(k)
+    B, H, N, d = q.shape
+    M, QB = N // 4, (N + 127) // 128
+    plan = absa.absa_plan_create(q.to(DEV), k.to(DEV), 30, 99, n_clusters=C, kmeans_iters=T,
+                                 keep_intermediates=True)
+    s = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M)
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * C).reshape(-1, C)
+    ref_s, _, ref_w = oracle.ibcs_scores(Q, K, n_clusters=C, iters=T)
+    bad = np.nonzero((w != ref_w.reshape(-1, C).astype(np.float32)).any(axis=1))[0]
+    assert flips_explained(Q, bad, N, C, T)
+    good = np.setdiff1d(np.arange(B * H * QB), bad)
+    assert score_error(s[good], ref_s.reshape(-1, M)[good]).max() <= SCORE_REL
+
+
+def test_minimal_shape():
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=4, d=64, seed=3))
+    plan = absa.absa_plan_create(q, k, 1, 5)
+    gp = plan.export()
+    assert list(gp["rowptr"]) == [0, 1] and list(gp["idx"]) == [0] and gp["p"][0] == 1.0
+    out = absa.absa_sparse_attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    check_output(to64(out), oracle.dense_attention(to64(q), to64(k), to64(v)), "N=4")
+
+
+def test_empty_rows_are_zero():
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=128, seed=4))
+    rowptr = np.array([0, 0, 3, 3, 5], np.int64)
+    idx = np.array([1, 7, 100, 0, 127], np.int32)
+    logw = np.array([0.0, 1.5, 0.2, 0.0, 3.0], np.float32)
+    plan = absa.absa_plan_import(rowptr, idx, logw, None, 1, 1, 512, 128)
+    out = absa.absa_sparse_attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    o = to64(out)
+    assert not o[0, 0, 0:128].any() and not o[0, 0, 256:384].any()
+    ref = oracle.plan_attention(to64(q), to64(k), to64(v), oracle_plan_of(
+        dict(rowptr=rowptr, idx=idx, logw=logw, p=np.exp(-logw.astype(np.float64))), 1, 1, 512, 128))
+    check_output(o, ref, "empty rows")
+
+
+def test_determinism():
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=3, N=2048, d=128, seed=8))
+    p1 = absa.absa_plan_create(q, k, 50, 17).export()
+    p2 = absa.absa_plan_create(q, k, 50, 17).export()
+    for key in p1:
+        assert np.array_equal(p1[key], p2[key]), key
+    p3 = absa.absa_plan_create(q, k, 50, 18).export()
+    assert not np.array_equal(p1["idx"], p3["idx"]) or not np.array_equal(p1["rowptr"], p3["rowptr"])
+    plan = absa.absa_plan_create(q, k, 50, 17)
+    o1 = absa.absa_sparse_attention(plan, q, k, v)
+    o2 = absa.absa_sparse_attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_plan_mismatch_and_bad_scores():
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=64, seed=9))
+    plan = absa.absa_plan_create(q, k, 10, 1)
+    q2 = q[:, :, :256].contiguous()
+    with pytest.raises(absa.AbsaError) as ei:
+        absa.absa_sparse_attention(plan, q2, q2, q2)
+    assert ei.value.status == absa.ABSA_ERR_PLAN_MISMATCH
+    s = torch.full((1, 1, 4, 128), 1.0 / 128, device=DEV)
+    absa.absa_plan_from_scores(s, 512, 64, 10, 1)
+    for bad in (float("nan"), 1.5, -0.25):
+        s2 = s.clone()
+        s2[0, 0, 2, 5] = bad
+        with pytest.raises(absa.AbsaError) as ei:
+            absa.absa_plan_from_scores(s2, 512, 64, 10, 1)
+        assert ei.value.status == absa.ABSA_ERR_INVALID_ARG
+    s3 = s.clone()
+    s3[0, 0, 1, :] = 1.0 / 64            # row sums to 2
+    with pytest.raises(absa.AbsaError):
+        absa.absa_plan_from_scores(s3, 512, 64, 10, 1)
+
+
+def test_allocation_failure_is_reported():
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=64, seed=10))
+    os.environ["ABSA_FAULT_INJECT"] = "alloc"
+    try:
+        with pytest.raises(absa.AbsaError) as ei:
+            absa.absa_plan_create(q, k, 10, 1)
+        assert ei.value.status == absa.ABSA_ERR_OUT_OF_MEMORY
+    finally:
+        del os.environ["ABSA_FAULT_INJECT"]
+    absa.absa_plan_create(q, k, 10, 1)       # works again
+
+
+def test_plan_reuse_over_denoising_steps():
+    # [hamidun, kernel paragraph]: the plan is rebuilt every 4 steps and the
+    # attention of the steps in between reuses it. Steps drift Q/K/V.
+    q, k, v = synth.make_inputs("small")
+    B, H, N, d = q.shape
+    budget = synth.budget_blocks(10, N // 4)
+    plan = absa.absa_plan_create(q.to(DEV), k.to(DEV), budget, synth.sip_seed(0))
+    gp = plan.export()
+    ref_plan = oracle_plan_of(gp, B, H, N, d)
+    for step in range(synth.REUSE_STEPS):
+        if step:
+            q, k, v = (synth.drift(x, seed=100 * step + i) for i, x in enumerate((q, k, v)))
+        out = absa.absa_sparse_attention(plan, q.to(DEV), k.to(DEV), v.to(DEV))
+        torch.cuda.synchronize()
+        hs = [0, H // 2, H - 1]
+        Q, K, V = to64(q)[:, hs], to64(k)[:, hs], to64(v)[:, hs]
+        sub = oracle.OraclePlan(B, len(hs), N, d, N // 4, (N + 127) // 128, *_subplan(gp, H, hs, N))
+        check_output(to64(out)[:, hs], oracle.plan_attention(Q, K, V, sub), f"step {step}")
+
+
+def _subplan(gp, H, hs, N):
+    QB = (N + 127) // 128
+    rowptr, idx, logw, p = [0], [], [], []
+    for h in hs:
+        for r in range(QB):
+            i = h * QB + r
+            lo, hi = gp["rowptr"][i], gp["rowptr"][i + 1]
+            idx.append(gp["idx"][lo:hi]); logw.append(gp["logw"][lo:hi]); p.append(gp["p"][lo:hi])
+            rowptr.append(rowptr[-1] + hi - lo)
+    return (np.array(rowptr, np.int64), np.concatenate(idx), np.concatenate(logw),
+            np.concatenate(p))
