@@ -1,0 +1,285 @@
+"""Benchmark of the AB-Attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan]
+
+A step is one pass of the whole hot path over the layer's Q/K/V, which are
+resident in HBM before timing starts: the plan (mean keys, IBCS k-means and
+scores, SIP probabilities, draws and CSR) followed by the gathered sparse
+attention. The dense flash-attention comparator is timed separately. Rank 0
+prints one JSON line. See the design doc for the definitions of every figure.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn ms & effective TFLOP/s per layer, 75.6K tok×40 heads, ~10% keep"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+ATTN_SOURCE = os.path.join(ROOT, "sampled_block_sparse_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attention_wan_traffic.txt")
+
+WORKLOADS = {
+    "wan": "Wan2.1-720p-like layer: B=1 H=40 N=75600 (21x45x80) d=128 bf16, budget 10%",
+    "hunyuan": "HunyuanVideo-720p-like layer: B=1 H=24 N=118800 (33x45x80) d=128 bf16, budget 8%",
+    "small": "small video-shaped layer: B=1 H=8 N=8192 (8x32x32) d=128 bf16, budget 10%",
+    "tiny": "tiny iid layer: B=1 H=2 N=1024 d=64 fp32, budget 25%",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan", choices=sorted(WORKLOADS))
+    ap.add_argument("--budget-pct", type=int, default=None)
+    ap.add_argument("--dense-iters", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy first (counter calibration)")
+    return ap.parse_args()
+
+
+def file_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per sparse-attention launch from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256") != file_sha256(ATTN_SOURCE):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def row_stats(rowptr, N, d, B, H):
+    """Useful and executed flop of one sparse-attention launch."""
+    QB = (N + 127) // 128
+    counts = np.diff(rowptr).reshape(B * H, QB)
+    n_r = np.minimum(128, N - 128 * np.arange(QB))          # real queries per row
+    useful = 4.0 * d * 4.0 * float((counts * n_r[None, :]).sum())
+    active_waves = (n_r + 31) // 32
+    tiles = (counts + 15) // 16
+    executed = 4.0 * d * 64.0 * 32.0 * float((tiles * active_waves[None, :]).sum())
+    return useful, executed, counts
+
+
+def cpu_baseline(q, k, v, budget, seed, seconds):
+    """The fp64 oracle on a bounded sample of plan rows of the same layer,
+    extrapolated to the whole layer."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    B, H, N, d = q.shape
+    QB, M = (N + 127) // 128, N // 4
+    rng = np.random.default_rng(0)
+    order = rng.permutation(B * H * QB)
+    t0 = time.perf_counter()
+    done = 0
+    heads = {}
+    kbar_time = 0.0
+    for row in order:
+        bh, r = divmod(int(row), QB)
+        b, h = divmod(bh, H)
+        if (b, h) not in heads:
+            Kh = k[b, h].float().numpy().astype(np.float64)
+            Vh = v[b, h].float().numpy().astype(np.float64)
+            t1 = time.perf_counter()
+            kb = oracle.mean_keys(Kh)
+            kbar_time += time.perf_counter() - t1
+            heads = {(b, h): (Kh, Vh, kb)}
+        Kh, Vh, kb = heads[(b, h)]
+        lo, hi = 128 * r, min(N, 128 * r + 128)
+        Qr = q[b, h, lo:hi].float().numpy().astype(np.float64)
+        s, _, _ = oracle.ibcs_row(Qr, kb)
+        p = oracle.sip_probabilities(s.astype(np.float32), budget)
+        idx, logw, _ = oracle.sip_draw_row(p, seed, b, h, r)
+        oracle.ht_attention_row(Qr, Kh, Vh, idx, logw)
+        done += 1
+        if time.perf_counter() - t0 >= seconds and done >= 4:
+            break
+    elapsed = time.perf_counter() - t0
+    per_row = (elapsed - kbar_time) / done
+    layer_s = per_row * B * H * QB + kbar_time * B * H / max(1, len(heads))
+    threads = 1
+    for pool in threadpool_info():
+        threads = max(threads, int(pool.get("num_threads", 1)))
+    return layer_s, done, elapsed, threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sampled_block_sparse_amd as absa
+    import synth
+
+    name = args.workload
+    cfg = synth.CONFIGS[name]
+    q, k, v = synth.make_inputs(name)
+    B, H, N, d = (int(x) for x in q.shape)
+    M = N // 4
+    pct = args.budget_pct if args.budget_pct is not None else cfg["budget_pct"]
+    budget = synth.budget_blocks(pct, M)
+    seed = synth.sip_seed(0)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    out = torch.empty_like(qd)
+    torch.cuda.synchronize()
+    print(f"[bench] workload={name} B={B} H={H} N={N} d={d} budget={budget} "
+          f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        plan = absa.absa_plan_create(qd, kd, budget, seed)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        absa.absa_sparse_attention(plan, qd, kd, vd, out)
+        ev1.record(stream)
+        return plan, ev0, ev1
+
+    for _ in range(args.warmup):
+        plan, _, _ = step()
+    torch.cuda.synchronize()
+
+    attn_events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan, e0, e1 = step()
+        attn_events.append((e0, e1))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms_all = [a.elapsed_time(b) for a, b in attn_events]
+    attn_ms = float(np.median(attn_ms_all))
+    attn_ms_mean = float(np.mean(attn_ms_all))
+    plan_ms = ms_per_step - attn_ms_mean
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, "
+          f"sparse attention {attn_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    # plan statistics and flop counts of one launch
+    gp = plan.export()
+    useful, executed, counts = row_stats(gp["rowptr"], N, d, B, H)
+    nnz = int(gp["rowptr"][-1])
+    keep_fraction = nnz / float(B * H * ((N + 127) // 128) * M)
+    dense_flop = 4.0 * B * H * float(N) * N * d
+
+    # dense comparator
+    dense_ms_all = []
+    dense_out = torch.empty_like(qd)
+    absa.absa_dense_attention(qd, kd, vd, dense_out)
+    for _ in range(args.dense_iters):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        absa.absa_dense_attention(qd, kd, vd, dense_out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms_all.append(e0.elapsed_time(e1))
+    dense_ms = float(np.median(dense_ms_all))
+    of, df = out.float(), dense_out.float()
+    rel_l2_vs_dense = float(torch.linalg.vector_norm(of - df) / torch.linalg.vector_norm(df))
+    del of, df
+
+    achieved = useful / (attn_ms * 1e-3) / 1e12
+    gathered_bytes = nnz * 2.0 * 4 * d * q.element_size()
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": read_traffic(),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a sample of rows", file=sys.stderr, flush=True)
+        layer_s, rows_done, elapsed, threads = cpu_baseline(q, k, v, budget, seed,
+                                                            args.cpu_seconds)
+        cpu = {
+            "value": round(dense_flop / layer_s / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{rows_done} random plan rows of the same layer (k-means, scores, SIP, "
+                       f"draws, HT attention) in {elapsed:.1f} s, extrapolated to all "
+                       f"{B * H * ((N + 127) // 128)} rows: {layer_s:.1f} s per layer"),
+        }
+
+    rec = {
+        "metric": METRIC,
+        "value": round(dense_flop / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded video-shaped Q/K/V generator)",
+        "config": {"workload": WORKLOADS[name] if pct == cfg["budget_pct"]
+                   else WORKLOADS[name].rsplit(",", 1)[0] + f", budget {pct}%",
+                   "B": B, "H": H, "N": N, "d": d, "budget_blocks": budget,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sparse_attn_ms": round(attn_ms, 4),
+        "sparse_attn_effective_tflops": round(dense_flop / (attn_ms * 1e-3) / 1e12, 2),
+        "sparse_attn_executed_tflops": round(executed / (attn_ms * 1e-3) / 1e12, 2),
+        "sparse_attn_useful_tflops": round(achieved, 2),
+        "frac_bf16_peak_executed": round(executed / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gathered_kv_GB": round(gathered_bytes / 1e9, 3),
+        "plan_ms": round(plan_ms, 4),
+        "amortized_ms_per_denoising_step": round(attn_ms + plan_ms / 4.0, 4),
+        "dense_ms": round(dense_ms, 4),
+        "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(dense_ms / attn_ms, 3),
+        "keep_fraction": round(keep_fraction, 5),
+        "rel_l2_vs_dense": round(rel_l2_vs_dense, 5),
+        "value_definition": "dense-equivalent flop 4*B*H*N^2*d per step / (plan + sparse attention) time",
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

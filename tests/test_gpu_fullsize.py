@@ -1,0 +1,107 @@
+"""GPU parity at the full layer sizes (Wan2.1-like 75,600 x 40 heads at 10%,
+HunyuanVideo-like 118,800 x 24 heads at 8%), in the launch configuration the
+bench times. The oracle recomputes a sample of plan rows one by one (scores,
+SIP draws given the GPU's scores, HT attention given the GPU's plan, dense
+rows); properties that hold at any size are checked on the whole plan."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sampled_block_sparse_amd as absa
+import synth
+from tests.gpu_util import SCORE_REL, check_output, score_error, to64, ulp_diff_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", params=["wan", "hunyuan"])
+def layer(request):
+    name = request.param
+    cfg = synth.CONFIGS[name]
+    print(f"[fullsize {name}] generating inputs", flush=True)
+    q, k, v = synth.make_inputs(name)
+    B, H, N, d = q.shape
+    M, QB = N // 4, (N + 127) // 128
+    budget = synth.budget_blocks(cfg["budget_pct"], M)
+    seed = synth.sip_seed(0)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    print(f"[fullsize {name}] plan + attention on the GPU", flush=True)
+    plan = absa.absa_plan_create(qd, kd, budget, seed, keep_intermediates=True)
+    out = absa.absa_sparse_attention(plan, qd, kd, vd)
+    dense = absa.absa_dense_attention(qd, kd, vd)
+    torch.cuda.synchronize()
+    gp = plan.export()
+    rows = [0, QB - 1, 3 * QB + QB // 2, (H - 1) * QB + QB - 1, (H // 2) * QB + 7,
+            (H - 1) * QB + 1]
+    scores = {r: plan.export_intermediate(absa.INTER_SCORES, r * M, M) for r in rows}
+    o_rows, d_rows = {}, {}
+    for r in rows:
+        h, rr = divmod(r, QB)
+        lo, hi = rr * 128, min(N, rr * 128 + 128)
+        o_rows[r] = to64(out[0, h, lo:hi])
+        d_rows[r] = to64(dense[0, h, lo:hi])
+    del qd, kd, vd, out, dense
+    plan.destroy()
+    torch.cuda.empty_cache()
+    return dict(name=name, q=q, k=k, v=v, B=B, H=H, N=N, d=d, M=M, QB=QB, budget=budget,
+                seed=seed, gp=gp, rows=rows, scores=scores, o_rows=o_rows, d_rows=d_rows)
+
+
+def _head(L, h):
+    return to64(L["k"][0, h]), to64(L["v"][0, h])
+
+
+def test_sampled_rows_match_oracle(layer):
+    L = layer
+    cache = {}
+    for row in L["rows"]:
+        h, r = divmod(row, L["QB"])
+        if h not in cache:
+            Kh, Vh = _head(L, h)
+            cache = {h: (Kh, Vh, oracle.mean_keys(Kh))}
+        Kh, Vh, kb = cache[h]
+        lo, hi = r * 128, min(L["N"], r * 128 + 128)
+        Qr = to64(L["q"][0, h, lo:hi])
+        # IBCS scores (an assignment near-tie is the only admissible divergence)
+        s_ref, _, _ = oracle.ibcs_row(Qr, kb)
+        err = score_error(L["scores"][row][None, :], s_ref[None, :])[0]
+        if err > SCORE_REL:
+            *_, margin = oracle.kmeans_block(Qr, 8, 4, return_margin=True)
+            assert margin < 1e-9, f"row {row}: score error {err:.2e}"
+        # SIP given the GPU's fp32 scores: bit-exact row of the plan
+        p = oracle.sip_probabilities(L["scores"][row], L["budget"])
+        idx, logw, pk = oracle.sip_draw_row(p, L["seed"], 0, h, r)
+        lo_p, hi_p = L["gp"]["rowptr"][row], L["gp"]["rowptr"][row + 1]
+        np.testing.assert_array_equal(L["gp"]["idx"][lo_p:hi_p], idx)
+        assert np.array_equal(L["gp"]["p"][lo_p:hi_p].view(np.uint64), pk.view(np.uint64))
+        assert (ulp_diff_f32(L["gp"]["logw"][lo_p:hi_p], logw) <= 1).all()
+        # HT attention given that plan row, and dense attention
+        check_output(L["o_rows"][row], oracle.ht_attention_row(Qr, Kh, Vh, idx, logw),
+                     f"{L['name']} row {row} sparse")
+        check_output(L["d_rows"][row], oracle.dense_attention_rows(Qr, Kh, Vh),
+                     f"{L['name']} row {row} dense")
+
+
+def test_whole_plan_properties(layer):
+    L = layer
+    gp = L["gp"]
+    rowptr, idx, logw, p = gp["rowptr"], gp["idx"], gp["logw"], gp["p"]
+    rows = L["B"] * L["H"] * L["QB"]
+    assert rowptr.shape == (rows + 1,) and rowptr[0] == 0
+    counts = np.diff(rowptr)
+    assert (counts >= 0).all() and (counts <= L["M"]).all()
+    assert ((idx >= 0) & (idx < L["M"])).all()
+    # strictly ascending inside each row
+    step = np.diff(idx.astype(np.int64))
+    inner = np.ones(idx.size, bool)
+    inner[rowptr[:-1][counts > 0]] = False          # first entry of each row
+    assert (step[inner[1:]] > 0).all()
+    # p in (0, 1]; logw is fp32(-ln p)
+    assert ((p > 0) & (p <= 1)).all()
+    expect = np.where(p == 1.0, 0.0, -np.log(p)).astype(np.float32)
+    assert (ulp_diff_f32(logw, expect) <= 1).all()
+    # Poisson sampling: the mean count per row is the budget
+    z = (counts.mean() - L["budget"]) / (np.sqrt(L["budget"] / rows))
+    assert abs(z) < 6, f"mean count {counts.mean():.2f} vs budget {L['budget']}"
