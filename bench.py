@@ -201,10 +201,11 @@ def main():
     keep_fraction = nnz / float(B * H * ((N + 127) // 128) * M)
     dense_flop = 4.0 * B * H * float(N) * N * d
 
-    # dense comparator
+    # dense comparator (skipped with --dense-iters 0)
     dense_ms_all = []
     dense_out = torch.empty_like(qd)
-    absa.absa_dense_attention(qd, kd, vd, dense_out)
+    if args.dense_iters > 0:
+        absa.absa_dense_attention(qd, kd, vd, dense_out)
     for _ in range(args.dense_iters):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -213,10 +214,12 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms_all.append(e0.elapsed_time(e1))
-    dense_ms = float(np.median(dense_ms_all))
-    of, df = out.float(), dense_out.float()
-    rel_l2_vs_dense = float(torch.linalg.vector_norm(of - df) / torch.linalg.vector_norm(df))
-    del of, df
+    dense_ms = float(np.median(dense_ms_all)) if dense_ms_all else None
+    rel_l2_vs_dense = None
+    if dense_ms_all:
+        of, df = out.float(), dense_out.float()
+        rel_l2_vs_dense = float(torch.linalg.vector_norm(of - df) / torch.linalg.vector_norm(df))
+        del of, df
 
     achieved = useful / (attn_ms * 1e-3) / 1e12
     gathered_bytes = nnz * 2.0 * 4 * d * q.element_size()
@@ -271,11 +274,11 @@ def main():
         "gathered_kv_GB": round(gathered_bytes / 1e9, 3),
         "plan_ms": round(plan_ms, 4),
         "amortized_ms_per_denoising_step": round(attn_ms + plan_ms / 4.0, 4),
-        "dense_ms": round(dense_ms, 4),
-        "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 2),
-        "speedup_vs_dense": round(dense_ms / attn_ms, 3),
+        "dense_ms": round(dense_ms, 4) if dense_ms else None,
+        "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
+        "speedup_vs_dense": round(dense_ms / attn_ms, 3) if dense_ms else None,
         "keep_fraction": round(keep_fraction, 5),
-        "rel_l2_vs_dense": round(rel_l2_vs_dense, 5),
+        "rel_l2_vs_dense": round(rel_l2_vs_dense, 5) if rel_l2_vs_dense is not None else None,
         "value_definition": "dense-equivalent flop 4*B*H*N^2*d per step / (plan + sparse attention) time",
     }
     print(json.dumps(rec), flush=True)
