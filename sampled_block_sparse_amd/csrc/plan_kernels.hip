@@ -60,22 +60,42 @@ __global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kb
 // left empty keeps its centroid. Outputs fp32 centroids [row, C, d] and
 // weights [row, C] = member share of the block's n queries under the last
 // assignment (C_eff = min(C, n); further clusters are zero with weight 0).
-// The centroid sums of bf16/fp32 inputs are exact in fp64, so each centroid
-// is the correctly rounded mean whatever the summation order.
+//
+// Layout: the queries stay in LDS in their storage type (bf16 or fp32, both
+// exact in fp64); thread (i, h) keeps query i in registers and computes its
+// distances to the CH clusters h*CH .. h*CH+CH-1 with CH independent fp64
+// FMA chains, reading the centroids from a [d][16] fp64 LDS array by
+// broadcast. The update ranks each cluster's members with wave ballots and
+// sums only members, so it costs n*d adds. The centroid sums of bf16/fp32
+// inputs are exact in fp64 for any realistic exponent spread, so each
+// centroid is the correctly rounded mean whatever the summation order.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T> struct QStore;
+template <> struct QStore<uint16_t> {
+    static constexpr int kPad = 2;            // odd row stride in 32-bit words
+    static __device__ __forceinline__ double get(const uint16_t* p) {
+        return static_cast<double>(bf16_to_f32(*p));
+    }
+};
+template <> struct QStore<float> {
+    static constexpr int kPad = 1;
+    static __device__ __forceinline__ double get(const float* p) { return static_cast<double>(*p); }
+};
+
+template <typename T, int D, int CH>
 __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, int64_t N,
-                                                     int64_t QB, int d, int C, int iters,
+                                                     int64_t QB, int C, int iters,
                                                      float* __restrict__ cent_out,
                                                      float* __restrict__ w_out) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int qstride = d + 1;                    // odd stride: conflict-free columns
-    float* qs = reinterpret_cast<float*>(smem);                                   // [128][d+1]
-    double* cs = reinterpret_cast<double*>(smem + ((kQueryBlock * qstride * 4 + 15) & ~15));  // [C][d]
+    constexpr int QS = D + QStore<T>::kPad;
+    __shared__ T qs[kQueryBlock * QS];
+    __shared__ __align__(16) double ct[D][2 * CH];      // centroids, transposed
     __shared__ double bdist[2][kQueryBlock];
     __shared__ int bidx[2][kQueryBlock];
     __shared__ int assign[kQueryBlock];
-    __shared__ int counts[kMaxClusters];
+    __shared__ int wcnt[2][2 * CH];
+    __shared__ int counts[2 * CH], offs[2 * CH];
+    __shared__ int members[kQueryBlock];
 
     const int64_t row = blockIdx.x;
     const int64_t bh = row / QB;
@@ -84,74 +104,101 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
     const int n = static_cast<int>(min<int64_t>(kQueryBlock, N - lo));
     const int ceff = min(C, n);
     const int tid = threadIdx.x;
-    const T* qrow = q + (bh * N + lo) * d;
+    const int lane = tid & 63, wave = tid >> 6;
+    const T* qrow = q + (bh * N + lo) * D;
 
-    for (int e = tid; e < n * d; e += blockDim.x) {
-        const int i = e / d, dd = e - i * d;
-        qs[i * qstride + dd] = load_f32(qrow + e);
+    for (int e = tid; e < n * D; e += blockDim.x) {
+        const int i = e / D, dd = e - i * D;
+        qs[i * QS + dd] = qrow[e];
     }
     __syncthreads();
-    for (int e = tid; e < ceff * d; e += blockDim.x) {
-        const int m = e / d, dd = e - m * d;
-        cs[e] = static_cast<double>(qs[((m * n) / ceff) * qstride + dd]);
+    for (int e = tid; e < D * 2 * CH; e += blockDim.x) {
+        const int dd = e / (2 * CH), m = e - dd * (2 * CH);
+        ct[dd][m] = (m < ceff) ? QStore<T>::get(&qs[((m * n) / ceff) * QS + dd]) : 0.0;
     }
     __syncthreads();
 
+    const int i = tid & (kQueryBlock - 1);
+    const int half = tid >> 7;
     for (int it = 0; it < iters; ++it) {
-        // Assignment: thread (i, half) scans clusters half, half+2, ...
-        {
-            const int i = tid & (kQueryBlock - 1);
-            const int half = tid >> 7;
-            if (i < n) {
-                double best = 0.0;
-                int bm = -1;
-                for (int m = half; m < ceff; m += 2) {
-                    double dist = 0.0;
-                    const float* qi = qs + i * qstride;
-                    const double* cm = cs + m * d;
-                    for (int dd = 0; dd < d; ++dd) {
-                        const double df = static_cast<double>(qi[dd]) - cm[dd];
-                        dist = fma(df, df, dist);
-                    }
-                    if (bm < 0 || dist < best) { best = dist; bm = m; }
+        // Distances of query i to clusters half*CH .. +CH-1.
+        if (i < n) {
+            double acc[CH];
+#pragma unroll
+            for (int m = 0; m < CH; ++m) acc[m] = 0.0;
+            const T* qi = qs + i * QS;
+#pragma unroll 4
+            for (int dd = 0; dd < D; ++dd) {
+                const double qv = QStore<T>::get(qi + dd);
+                const double* cr = &ct[dd][half * CH];
+#pragma unroll
+                for (int m = 0; m < CH; ++m) {
+                    const double df = qv - cr[m];
+                    acc[m] = fma(df, df, acc[m]);
                 }
-                bdist[half][i] = best;
-                bidx[half][i] = bm;
+            }
+            double best = 0.0;
+            int bm = -1;
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                const int mm = half * CH + m;
+                if (mm < ceff && (bm < 0 || acc[m] < best)) { best = acc[m]; bm = mm; }
+            }
+            bdist[half][i] = best;
+            bidx[half][i] = bm;
+        }
+        __syncthreads();
+        // Combine the halves (ties to the smaller index) and rank members.
+        if (tid < kQueryBlock) {
+            int a = -1;
+            if (tid < n) {
+                a = bidx[0][tid];
+                const int m1 = bidx[1][tid];
+                if (m1 >= 0 && (a < 0 || bdist[1][tid] < bdist[0][tid])) a = m1;
+                assign[tid] = a;
+            }
+            int rank = 0;
+            for (int m = 0; m < ceff; ++m) {
+                const uint64_t b = __ballot(a == m);
+                if (a == m) rank = __popcll(b & ((1ull << lane) - 1ull));
+                if (lane == 0) wcnt[wave][m] = __popcll(b);
+            }
+            bdist[0][tid] = static_cast<double>(rank);      // reuse as scratch
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int o = 0;
+            for (int m = 0; m < ceff; ++m) {
+                offs[m] = o;
+                counts[m] = wcnt[0][m] + wcnt[1][m];
+                o += counts[m];
             }
         }
         __syncthreads();
         if (tid < n) {
-            int a = bidx[0][tid];
-            const int m1 = bidx[1][tid];
-            if (m1 >= 0) {
-                const double d0 = bdist[0][tid], d1 = bdist[1][tid];
-                if (d1 < d0 || (d1 == d0 && m1 < a)) a = m1;
-            }
-            assign[tid] = a;
+            const int a = assign[tid];
+            const int pos = offs[a] + (tid >= 64 ? wcnt[0][a] : 0) + static_cast<int>(bdist[0][tid]);
+            members[pos] = tid;
         }
         __syncthreads();
-        if (tid < ceff) {
-            int cnt = 0;
-            for (int i = 0; i < n; ++i) cnt += (assign[i] == tid);
-            counts[tid] = cnt;
-        }
         // Update: each (cluster, channel) pair owned by one thread.
-        for (int e = tid; e < ceff * d; e += blockDim.x) {
-            const int m = e / d, dd = e - m * d;
-            double s = 0.0;
-            int cnt = 0;
-            for (int i = 0; i < n; ++i) {
-                if (assign[i] == m) { s += static_cast<double>(qs[i * qstride + dd]); ++cnt; }
+        for (int e = tid; e < ceff * D; e += blockDim.x) {
+            const int m = e / D, dd = e - m * D;
+            const int cnt = counts[m];
+            if (cnt) {
+                const int* mem = members + offs[m];
+                double sum = 0.0;
+                for (int k = 0; k < cnt; ++k) sum += QStore<T>::get(&qs[mem[k] * QS + dd]);
+                ct[dd][m] = sum / static_cast<double>(cnt);
             }
-            if (cnt) cs[e] = s / static_cast<double>(cnt);
         }
         __syncthreads();
     }
 
-    float* co = cent_out + row * C * d;
-    for (int e = tid; e < C * d; e += blockDim.x) {
-        const int m = e / d;
-        co[e] = (m < ceff) ? static_cast<float>(cs[e]) : 0.0f;
+    float* co = cent_out + row * C * D;
+    for (int e = tid; e < C * D; e += blockDim.x) {
+        const int m = e / D, dd = e - m * D;
+        co[e] = (m < ceff) ? static_cast<float>(ct[dd][m]) : 0.0f;
     }
     if (tid < C) {
         w_out[row * C + tid] = (tid < ceff)
@@ -313,22 +360,22 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide reductions (256 threads = 4 waves).
+// Block-wide reductions.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+template <typename V> __device__ __forceinline__ V wave_sum(V v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
 
-__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
-    v = wave_sum_u64(v);
+template <typename V> __device__ V block_sum(V v, V* red) {
+    v = wave_sum(v);
     const int wave = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
-    uint64_t t = 0;
-    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) t += red[i];
+    V t = 0;
+    for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) t += red[k];
     return t;
 }
 
@@ -361,48 +408,65 @@ __device__ __forceinline__ double sip_uniform(uint64_t seed, int64_t b, int64_t 
     return static_cast<double>(u53) * 0x1.0p-53;
 }
 
-__device__ __forceinline__ uint64_t fixed_point(float s) {
-    return static_cast<uint64_t>(floor(static_cast<double>(s) * 0x1.0p52));
+// floor(s * 2^52) of an fp32 score in [0, 1], as an exact fp64 integer. Sums
+// of such integers below 2^53 are exact in fp64 in any order, which is the
+// order-free fixed-point arithmetic the sampler's rule asks for.
+__device__ __forceinline__ double fixed_point(float s) {
+    return floor(static_cast<double>(s) * 0x1.0p52);
 }
 
-// p of block j given the row's outcome. capped blocks have p = 1.
-__device__ __forceinline__ double sip_p(bool capped, const SipRow& ri, uint64_t q) {
+// p of block j given the row's outcome; capped blocks have p = 1.
+__device__ __forceinline__ double sip_p(bool capped, const SipRow& ri, float s) {
     if (capped || ri.mode == 0) return 1.0;
     if (ri.mode == 1) return ri.c;
-    return ri.c * static_cast<double>(q);
+    return ri.c * fixed_point(s);
 }
 
 // ---------------------------------------------------------------------------
-// SIP probabilities and draw count [hamidun, SIP paragraph; edumints, SIP
-// item]: capped water-filling in exact fixed point (q_j = floor(s_j 2^52),
-// integer sums, IEEE double division and product), then one Poisson draw per
-// block. One workgroup per plan row. The cap mask (one bit per block) and the
-// final multiplier go to global memory for the fill kernel.
+// SIP probabilities and draws [hamidun, SIP paragraph; edumints, SIP item]:
+// capped water-filling in exact fixed point (q_j = floor(s_j 2^52), exact
+// sums, IEEE double division and product), then one Poisson draw per block.
+// One workgroup per plan row. With LDS_ROW the row's scores live in LDS and a
+// capped block is marked by negating its score; otherwise the scores are
+// re-read from global memory and caps kept in the global cap mask. The
+// kernel writes the row's cap and keep masks (one bit per block), its count
+// and the final multiplier.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void sip_count_kernel(
+constexpr int kSipThreads = 512;
+constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
+
+template <bool LDS_ROW>
+__global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
-    uint64_t seed, uint64_t* __restrict__ capmask, SipRow* __restrict__ rowinfo,
-    int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
-    __shared__ uint64_t red[4];
+    uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
+    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    extern __shared__ float sv[];
+    __shared__ double redd[kSipThreads / 64];
+    __shared__ int redi[kSipThreads / 64];
     const int64_t row = blockIdx.x;
-    const float* s = scores + row * M;
+    const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
     uint64_t* cm = capmask + row * words;
+    uint64_t* km = keepmask + row * words;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane = tid & 63, wave = tid >> 6;
 
-    uint64_t sum = 0, bad = 0;
-    for (int64_t j = tid; j < M; j += 256) {
-        const float v = s[j];
+    double sum = 0.0;
+    int bad = 0;
+    for (int64_t j = tid; j < M; j += kSipThreads) {
+        const float v = sg[j];
         if (!(v >= 0.0f && v <= 1.0f)) bad = 1;
         else sum += fixed_point(v);
+        if (LDS_ROW) sv[j] = v;
     }
-    // each 64-block word is owned by the wave that later tests and sets it
-    for (int64_t base = 0; base < M; base += 256)
-        if (lane == 0 && base + tid < M) cm[(base + tid) >> 6] = 0;
-    const uint64_t total = block_sum_u64(sum, red);
-    const uint64_t nbad = block_sum_u64(bad, red);
-    if (nbad != 0 || total >= (1ull << 53)) {
+    if (!LDS_ROW) {
+        // each 64-block word is owned by the wave that later tests and sets it
+        for (int64_t base = 0; base < M; base += kSipThreads)
+            if (lane == 0 && base + wave * 64 < M) cm[(base >> 6) + wave] = 0;
+    }
+    const double total = block_sum(sum, redd);
+    const int nbad = block_sum(bad, redi);
+    if (nbad != 0 || total >= 0x1.0p53) {
         if (tid == 0) {
             status->bad_scores = 1;
             counts[row] = 0;
@@ -413,37 +477,51 @@ __global__ __launch_bounds__(256) void sip_count_kernel(
     }
 
     int64_t taken = 0, n_active = M;
-    uint64_t S = total;
+    double S = total;
     SipRow ri;
     ri.pad = 0;
     for (;;) {
         const int64_t left = budget - taken;
         if (left >= n_active) { ri.mode = 0; ri.c = 1.0; break; }
-        if (S == 0) {
+        if (S == 0.0) {
             ri.mode = 1;
             ri.c = static_cast<double>(left) / static_cast<double>(n_active);
             break;
         }
-        const double c = static_cast<double>(left) / static_cast<double>(S);
-        uint64_t ncap = 0, scap = 0;
-        for (int64_t base = 0; base < M; base += 256) {
+        const double c = static_cast<double>(left) / S;
+        int ncap = 0;
+        double scap = 0.0;
+        for (int64_t base = 0; base < M; base += kSipThreads) {
             const int64_t j = base + tid;
             bool hit = false;
-            uint64_t q = 0;
+            double dq = 0.0;
             if (j < M) {
-                const bool was = (cm[j >> 6] >> (j & 63)) & 1ull;
-                q = fixed_point(s[j]);
-                hit = !was && (c * static_cast<double>(q) >= 1.0);
+                if (LDS_ROW) {
+                    const float v = sv[j];
+                    if (v >= 0.0f) {
+                        dq = fixed_point(v);
+                        hit = c * dq >= 1.0;
+                        if (hit) sv[j] = -v;
+                    }
+                } else {
+                    const bool was = (cm[j >> 6] >> (j & 63)) & 1ull;
+                    if (!was) {
+                        dq = fixed_point(sg[j]);
+                        hit = c * dq >= 1.0;
+                    }
+                }
             }
-            const uint64_t ballot = __ballot(hit);
-            if (hit) { ++ncap; scap += q; }
-            if (lane == 0 && ballot) cm[j >> 6] |= ballot;
+            if (!LDS_ROW) {
+                const uint64_t bal = __ballot(hit);
+                if (lane == 0 && bal) cm[j >> 6] |= bal;
+            }
+            if (hit) { ++ncap; scap += dq; }
         }
-        const uint64_t tcap = block_sum_u64(ncap, red);
-        const uint64_t tsum = block_sum_u64(scap, red);
+        const int tcap = block_sum(ncap, redi);
+        const double tsum = block_sum(scap, redd);
         if (tcap == 0) { ri.mode = 2; ri.c = c; break; }
-        taken += static_cast<int64_t>(tcap);
-        n_active -= static_cast<int64_t>(tcap);
+        taken += tcap;
+        n_active -= tcap;
         S -= tsum;
     }
 
@@ -451,15 +529,33 @@ __global__ __launch_bounds__(256) void sip_count_kernel(
     const int64_t r = row - bidx * QB;
     const int64_t h = bidx % H;
     const int64_t b = bidx / H;
-    uint64_t kept = 0;
-    for (int64_t j = tid; j < M; j += 256) {
-        const bool capped = (cm[j >> 6] >> (j & 63)) & 1ull;
-        const double p = sip_p(capped, ri, fixed_point(s[j]));
-        kept += (sip_uniform(seed, b, h, r, j) < p) ? 1 : 0;
+    int kept = 0;
+    for (int64_t base = 0; base < M; base += kSipThreads) {
+        const int64_t j = base + tid;
+        bool keep = false, capped = false;
+        if (j < M) {
+            float v;
+            if (LDS_ROW) {
+                v = sv[j];
+                capped = v < 0.0f;
+                v = fabsf(v);
+            } else {
+                capped = (cm[j >> 6] >> (j & 63)) & 1ull;
+                v = sg[j];
+            }
+            keep = sip_uniform(seed, b, h, r, j) < sip_p(capped, ri, v);
+        }
+        const uint64_t kb = __ballot(keep);
+        const uint64_t cb = __ballot(capped);
+        if (lane == 0 && base + wave * 64 < M) {
+            km[(base >> 6) + wave] = kb;
+            if (LDS_ROW) cm[(base >> 6) + wave] = cb;
+        }
+        kept += keep ? 1 : 0;
     }
-    const uint64_t tk = block_sum_u64(kept, red);
+    const int tk = block_sum(kept, redi);
     if (tid == 0) {
-        counts[row] = static_cast<int64_t>(tk);
+        counts[row] = tk;
         rowinfo[row] = ri;
     }
 }
@@ -498,48 +594,53 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
     }
 }
 
-// Fill the CSR row: ascending kept block indices, fp32 log-weights -ln p
-// (+0 for p = 1), and p. Order-preserving compaction with wave ballots.
+// Fill the CSR row from the keep mask: ascending kept block indices, fp32
+// log-weights -ln p (+0 for p = 1), and p. Thread t owns keep-mask word t of
+// a 256-word chunk; an exclusive scan of the words' popcounts gives each
+// thread the position of its first kept block.
 __global__ __launch_bounds__(256) void sip_fill_kernel(
-    const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, uint64_t seed,
-    const uint64_t* __restrict__ capmask, const SipRow* __restrict__ rowinfo,
+    const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
+    const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
     const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
     double* __restrict__ p_out) {
-    __shared__ int64_t wcount[4];
+    __shared__ int wtot[4];
     const int64_t row = blockIdx.x;
-    const float* s = scores + row * M;
+    const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
     const uint64_t* cm = capmask + row * words;
+    const uint64_t* km = keepmask + row * words;
     const SipRow ri = rowinfo[row];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t bidx = row / QB;
-    const int64_t r = row - bidx * QB;
-    const int64_t h = bidx % H;
-    const int64_t b = bidx / H;
     int64_t pos = rowptr[row];
-    for (int64_t base = 0; base < M; base += 256) {
-        const int64_t j = base + tid;
-        bool keep = false;
-        double p = 0.0;
-        if (j < M) {
-            const bool capped = (cm[j >> 6] >> (j & 63)) & 1ull;
-            p = sip_p(capped, ri, fixed_point(s[j]));
-            keep = sip_uniform(seed, b, h, r, j) < p;
+    for (int64_t base = 0; base < words; base += 256) {
+        const int64_t w = base + tid;
+        const uint64_t kw = (w < words) ? km[w] : 0ull;
+        const uint64_t cw = (w < words) ? cm[w] : 0ull;
+        const int pc = __popcll(kw);
+        int incl = pc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
         }
-        const uint64_t ballot = __ballot(keep);
-        const int before = __popcll(ballot & ((1ull << lane) - 1ull));
-        if (lane == 0) wcount[wave] = __popcll(ballot);
+        if (lane == 63) wtot[wave] = incl;
         __syncthreads();
-        int64_t woff = 0, tot = 0;
+        int woff = 0, tot = 0;
         for (int k = 0; k < 4; ++k) {
-            if (k < wave) woff += wcount[k];
-            tot += wcount[k];
+            if (k < wave) woff += wtot[k];
+            tot += wtot[k];
         }
-        if (keep) {
-            const int64_t at = pos + woff + before;
+        int64_t at = pos + woff + incl - pc;
+        uint64_t bits = kw;
+        while (bits) {
+            const int bit = __ffsll(static_cast<long long>(bits)) - 1;
+            bits &= bits - 1;
+            const int64_t j = w * 64 + bit;
+            const double p = sip_p((cw >> bit) & 1ull, ri, sg[j]);
             idx[at] = static_cast<int32_t>(j);
             logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
             p_out[at] = p;
+            ++at;
         }
         pos += tot;
         __syncthreads();
@@ -570,25 +671,28 @@ hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int 
     });
 }
 
+template <typename T, int D>
+static void launch_kmeans_t(const void* q, int64_t BH, int64_t N, int C, int iters, float* cent,
+                            float* w, hipStream_t s) {
+    const int64_t QB = (N + kQueryBlock - 1) / kQueryBlock;
+    if (C <= 8)
+        hipLaunchKernelGGL((kmeans_kernel<T, D, 4>), dim3(BH * QB), dim3(256), 0, s,
+                           static_cast<const T*>(q), N, QB, C, iters, cent, w);
+    else
+        hipLaunchKernelGGL((kmeans_kernel<T, D, 8>), dim3(BH * QB), dim3(256), 0, s,
+                           static_cast<const T*>(q), N, QB, C, iters, cent, w);
+}
+
 hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d, int C,
                          int iters, float* cent, float* w, hipStream_t s) {
-    const int64_t QB = (N + kQueryBlock - 1) / kQueryBlock;
-    const size_t qbytes = (static_cast<size_t>(kQueryBlock) * (d + 1) * 4 + 15) & ~size_t(15);
-    const size_t shm = qbytes + static_cast<size_t>(C) * d * 8;
-    // up to 82 KB of dynamic LDS at d = 128 (gfx950 has 160 KB per CU)
-    hipError_t e = (dt == kBF16)
-        ? hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_kernel<uint16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm))
-        : hipFuncSetAttribute(reinterpret_cast<const void*>(&kmeans_kernel<float>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e != hipSuccess) return e;
     return launch_checked([&] {
-        if (dt == kBF16)
-            hipLaunchKernelGGL(kmeans_kernel<uint16_t>, dim3(BH * QB), dim3(256), shm, s,
-                               static_cast<const uint16_t*>(q), N, QB, d, C, iters, cent, w);
-        else
-            hipLaunchKernelGGL(kmeans_kernel<float>, dim3(BH * QB), dim3(256), shm, s,
-                               static_cast<const float*>(q), N, QB, d, C, iters, cent, w);
+        if (dt == kBF16) {
+            if (d == 128) launch_kmeans_t<uint16_t, 128>(q, BH, N, C, iters, cent, w, s);
+            else launch_kmeans_t<uint16_t, 64>(q, BH, N, C, iters, cent, w, s);
+        } else {
+            if (d == 128) launch_kmeans_t<float, 128>(q, BH, N, C, iters, cent, w, s);
+            else launch_kmeans_t<float, 64>(q, BH, N, C, iters, cent, w, s);
+        }
     });
 }
 
@@ -620,14 +724,24 @@ hipError_t launch_scores(const float* cent, const float* w, const float* kbar, i
 }
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
-                            int64_t budget, uint64_t seed, uint32_t* capmask, SipRow* rowinfo,
-                            int64_t* counts, PlanStatus* status, hipStream_t s) {
-    (void)B;
+                            int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
+                            SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
+    if (M <= kSipLdsMaxBlocks) {
+        const size_t shm = static_cast<size_t>(M) * sizeof(float);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sip_count_kernel<true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(kSipLdsMaxBlocks * sizeof(float)));
+        if (e != hipSuccess) return e;
+        return launch_checked([&] {
+            hipLaunchKernelGGL(sip_count_kernel<true>, dim3(rows), dim3(kSipThreads), shm, s,
+                               scores, H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts,
+                               status);
+        });
+    }
     return launch_checked([&] {
-        hipLaunchKernelGGL(sip_count_kernel, dim3(rows), dim3(256), 0, s, scores, H, QB, M,
-                           budget, seed, reinterpret_cast<uint64_t*>(capmask), rowinfo, counts,
-                           status);
+        hipLaunchKernelGGL(sip_count_kernel<false>, dim3(rows), dim3(kSipThreads), 0, s, scores,
+                           H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts, status);
     });
 }
 
@@ -638,15 +752,12 @@ hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr, Pla
     });
 }
 
-hipError_t launch_sip_fill(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
-                           uint64_t seed, const uint32_t* capmask, const SipRow* rowinfo,
-                           const int64_t* rowptr, int32_t* idx, float* logw, double* p,
-                           hipStream_t s) {
-    const int64_t rows = B * H * QB;
+hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M, const uint64_t* capmask,
+                           const uint64_t* keepmask, const SipRow* rowinfo, const int64_t* rowptr,
+                           int32_t* idx, float* logw, double* p, hipStream_t s) {
     return launch_checked([&] {
-        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, H, QB, M, seed,
-                           reinterpret_cast<const uint64_t*>(capmask), rowinfo, rowptr, idx,
-                           logw, p);
+        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, capmask,
+                           keepmask, rowinfo, rowptr, idx, logw, p);
     });
 }
 
