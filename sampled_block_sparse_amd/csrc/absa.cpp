@@ -238,16 +238,18 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
 
     absa_status st = [&]() -> absa_status {
         DeviceArena arena;
+        uint16_t* kbar3 = nullptr;
         ABSA_TRY(arena.alloc(&P->kbar, B * H * M * d, "mean keys"));
+        ABSA_TRY(arena.alloc(&kbar3, B * H * M * 3 * d, "split mean keys"));
         ABSA_TRY(arena.alloc(&P->cent, P->rows * C * d, "centroids"));
         ABSA_TRY(arena.alloc(&P->w, P->rows * C, "cluster weights"));
         ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
-        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), P->kbar, s),
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), P->kbar, kbar3, s),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
                                P->cent, P->w, s),
                  "k-means kernel");
-        ABSA_HIP(launch_scores(P->cent, P->w, P->kbar, B * H, P->QB, M, static_cast<int>(d), C,
+        ABSA_HIP(launch_scores(P->cent, P->w, kbar3, B * H, P->QB, M, static_cast<int>(d), C,
                                P->scores, s),
                  "score kernel");
         ABSA_TRY(run_sip(P, P->scores, params->budget_blocks, params->seed, s, arena));

@@ -34,13 +34,15 @@ struct PlanStatus {
     int32_t pad;
 };
 
+// kbar: fp32 means [BH, M, d]; kbar3: their exact three-way bf16 split
+// [BH, M, 3, d] (hi, mid, lo planes), the score kernel's operand.
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, hipStream_t s);
+                            float* kbar, uint16_t* kbar3, hipStream_t s);
 
 hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
                          int C, int iters, float* cent, float* w, hipStream_t s);
 
-hipError_t launch_scores(const float* cent, const float* w, const float* kbar,
+hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3,
                          int64_t BH, int64_t QB, int64_t M, int d, int C,
                          float* scores, hipStream_t s);
 

@@ -28,14 +28,32 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
+// Split of an fp32 value into three bf16 values hi + mid + lo == x (exact for
+// normal x: each step removes the 8 leading significant bits, and the
+// subtractions are exact).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    const __bf16 h = static_cast<__bf16>(x);
+    const float r1 = x - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);
+    const __bf16 l = static_cast<__bf16>(r2);
+    hi = __builtin_bit_cast(uint16_t, h);
+    mid = __builtin_bit_cast(uint16_t, m);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// ---------------------------------------------------------------------------
 // Mean keys [hamidun, IBCS paragraph: "averaged keys"]:
 // kbar[bh, j, :] = (k[bh, 4j] + k[bh, 4j+1] + k[bh, 4j+2] + k[bh, 4j+3]) / 4.
 // One thread per (bh, j, 4-channel chunk); the fp32 sum of four bf16 values
-// is exact unless their exponents differ by more than 15.
+// is exact unless their exponents differ by more than 15. Also writes the
+// three-way bf16 split of each mean, kbar3[bh, j, plane, :], the operand of
+// the score kernel's matrix products.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kbar,
-                                 int64_t chunks, int d) {
+                                 uint16_t* __restrict__ kbar3, int64_t chunks, int d) {
     const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (c >= chunks) return;
     const int per_row = d >> 2;
@@ -48,8 +66,18 @@ __global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kb
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += load_f32(src + t * d + e);
     }
-    float4 out = make_float4(acc[0] * 0.25f, acc[1] * 0.25f, acc[2] * 0.25f, acc[3] * 0.25f);
-    *reinterpret_cast<float4*>(kbar + blk * d + d0) = out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= 0.25f;
+    *reinterpret_cast<float4*>(kbar + blk * d + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    uint16_t pl[3][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split3_bf16(acc[e], pl[0][e], pl[1][e], pl[2][e]);
+    uint16_t* dst = kbar3 + blk * 3 * d + d0;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<uint2*>(dst + q * d) =
+            make_uint2(pl[q][0] | (static_cast<uint32_t>(pl[q][1]) << 16),
+                       pl[q][2] | (static_cast<uint32_t>(pl[q][3]) << 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -210,30 +238,39 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // ---------------------------------------------------------------------------
 // IBCS scores [hamidun, IBCS paragraph]: for each query block r and KV block
 // j, s_j = sum_m w_m * softmax_j(c_m . kbar_j / sqrt(d)), softmax over all M
-// KV blocks of the head. This is a dense fp32 contraction
-// (centroids x mean keys, per head) and runs on fp32 MFMA 32x32x2:
-// a wave owns 32 centroid slots (32/CP query blocks of CP slots; slots past C
-// have weight 0) against 32-key tiles staged in LDS. Pass 1 keeps per-lane
-// running (max, sum) of each centroid's exponentials and merges them across
-// lanes; pass 2 recomputes the logits and writes the weighted sum over the
-// block's clusters. MFMA D layout (32x32): lane l holds column l%32 and rows
-// (i/4)*8 + (l/32)*4 + i%4 for i < 16.
+// KV blocks of the head. This is a dense contraction (centroids x mean keys,
+// per head) that must be fp32-accurate; it runs on the bf16 MFMA
+// (32x32x16) with both operands split three ways, c = c1 + c2 + c3 and
+// kbar = k1 + k2 + k3, summing the six products c1k1, c1k2, c2k1, c1k3,
+// c2k2, c3k1 (the three dropped ones are below 2^-24 of the result); each
+// bf16 product is exact in fp32 and accumulates in fp32, c1k1 in its own
+// accumulator. A wave owns 32 centroid slots (32/CP query blocks of CP
+// slots; slots past C have weight 0) against 32-key tiles staged in LDS.
+// Pass 1 keeps per-lane running (max, sum) of each centroid's exponentials
+// and merges them across lanes; pass 2 recomputes the logits and writes the
+// weighted sum over the block's clusters. MFMA D layout (32x32): lane l
+// holds column l%32 (a key) and rows (i/4)*8 + (l/32)*4 + i%4 (centroid
+// slots) for i < 16.
 // ---------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTile = 32;
 
 template <int CP, int D>
-__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ cent,
-                                                     const float* __restrict__ w,
-                                                     const float* __restrict__ kbar,
-                                                     int64_t QB, int64_t M, int C,
-                                                     float scale_log2,
-                                                     float* __restrict__ scores) {
+__global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict__ cent,
+                                                        const float* __restrict__ w,
+                                                        const uint16_t* __restrict__ kbar3,
+                                                        int64_t QB, int64_t M, int C,
+                                                        float scale_log2,
+                                                        float* __restrict__ scores) {
     constexpr int RPW = 32 / CP;                    // query blocks per wave
-    constexpr int KS = D + 2;                       // LDS row stride (floats)
-    __shared__ __align__(16) float ks[kScoreTile * KS];
+    constexpr int NSTEP = D / 16;                   // MFMA k-steps
+    constexpr int KROW = 3 * D + 8;                 // LDS key row (bf16), padded
+    constexpr int CHUNKS = kScoreTile * 3 * D / 8;  // 16-byte chunks per tile
+    constexpr int CPT = CHUNKS / 256;               // per thread
+    __shared__ __align__(16) uint16_t ks[kScoreTile * KROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -243,37 +280,75 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
     const int64_t bh = blockIdx.y;
     const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * kScoreWaves + wave) * RPW;
 
-    // A operand: this lane's centroid slot (row col of the 32x32 block).
+    // A operands: this lane's centroid slot (row col of the 32x32 block),
+    // channels s*16 + half*8 .. +8 of each step, in three bf16 planes.
     const int64_t my_r = r0 + col / CP;
     const int my_m = col % CP;
     const bool slot_ok = (my_r < QB) && (my_m < C);
-    float a[D / 2];
+    uint4 a1[NSTEP], a2[NSTEP], a3[NSTEP];
     {
         const float* src = cent + ((bh * QB + my_r) * C + my_m) * D;
 #pragma unroll
-        for (int s = 0; s < D / 2; ++s) a[s] = slot_ok ? src[2 * s + half] : 0.0f;
+        for (int st = 0; st < NSTEP; ++st) {
+            uint16_t hv[8], mv[8], lv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = slot_ok ? src[st * 16 + half * 8 + e] : 0.0f;
+                split3_bf16(x, hv[e], mv[e], lv[e]);
+            }
+            auto pack = [](const uint16_t (&v)[8]) {
+                return make_uint4(v[0] | (static_cast<uint32_t>(v[1]) << 16),
+                                  v[2] | (static_cast<uint32_t>(v[3]) << 16),
+                                  v[4] | (static_cast<uint32_t>(v[5]) << 16),
+                                  v[6] | (static_cast<uint32_t>(v[7]) << 16));
+            };
+            a1[st] = pack(hv);
+            a2[st] = pack(mv);
+            a3[st] = pack(lv);
+        }
     }
 
-    const float* kb = kbar + bh * M * D;
+    const uint16_t* kb = kbar3 + bh * M * 3 * D;
     const int64_t ntiles = (M + kScoreTile - 1) / kScoreTile;
+    uint4 pre[CPT];
 
-    auto load_tile = [&](int64_t t) {
+    auto fetch_tile = [&](int64_t t) {
         const int64_t j0 = t * kScoreTile;
-        for (int e = tid * 4; e < kScoreTile * D; e += 256 * 4) {
-            const int key = e / D, dd = e - key * D;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 + key < M) v = *reinterpret_cast<const float4*>(kb + (j0 + key) * D + dd);
-            float* dst = ks + key * KS + dd;
-            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int e = tid + 256 * i;
+            const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
+            pre[i] = (j0 + key < M)
+                ? *reinterpret_cast<const uint4*>(kb + (j0 + key) * 3 * D + c8 * 8)
+                : make_uint4(0, 0, 0, 0);
         }
     };
-    auto tile_logits = [&]() {
-        floatx16 acc = {};
+    auto store_tile = [&]() {
 #pragma unroll
-        for (int s = 0; s < D / 2; ++s) {
-            const float b = ks[col * KS + 2 * s + half];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b, acc, 0, 0, 0);
+        for (int i = 0; i < CPT; ++i) {
+            const int e = tid + 256 * i;
+            const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
+            *reinterpret_cast<uint4*>(&ks[key * KROW + c8 * 8]) = pre[i];
         }
+    };
+    auto as8 = [](uint4 u) { return __builtin_bit_cast(bf16x8, u); };
+    auto tile_logits = [&]() {
+        floatx16 acc = {}, acc2 = {};
+        const uint16_t* kr = &ks[col * KROW + half * 8];
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            const bf16x8 b1 = as8(*reinterpret_cast<const uint4*>(kr + st * 16));
+            const bf16x8 b2 = as8(*reinterpret_cast<const uint4*>(kr + D + st * 16));
+            const bf16x8 b3 = as8(*reinterpret_cast<const uint4*>(kr + 2 * D + st * 16));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, acc, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b2, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b3, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b1, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b2, acc2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += acc2[i];
         return acc;
     };
 
@@ -281,17 +356,19 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
     float mx[16], zs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { mx[i] = -INFINITY; zs[i] = 0.0f; }
+    fetch_tile(0);
     for (int64_t t = 0; t < ntiles; ++t) {
         __syncthreads();
-        load_tile(t);
+        store_tile();
         __syncthreads();
+        if (t + 1 < ntiles) fetch_tile(t + 1);
         const floatx16 acc = tile_logits();
         if (t * kScoreTile + col < M) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float x = acc[i] * scale_log2;
                 const float mn = fmaxf(mx[i], x);
-                zs[i] = zs[i] * exp2f(mx[i] - mn) + exp2f(x - mn);
+                zs[i] = zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn) + __builtin_amdgcn_exp2f(x - mn);
                 mx[i] = mn;
             }
         }
@@ -304,8 +381,8 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
             const float m2 = __shfl_xor(mx[i], off);
             const float z2 = __shfl_xor(zs[i], off);
             const float mn = fmaxf(mx[i], m2);
-            const float e1 = (mx[i] == -INFINITY) ? 0.0f : zs[i] * exp2f(mx[i] - mn);
-            const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * exp2f(m2 - mn);
+            const float e1 = (mx[i] == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn);
+            const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * __builtin_amdgcn_exp2f(m2 - mn);
             zs[i] = e1 + e2;
             mx[i] = mn;
         }
@@ -323,10 +400,12 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
     }
 
     // Pass 2: weighted sum over each query block's clusters.
+    fetch_tile(0);
     for (int64_t t = 0; t < ntiles; ++t) {
         __syncthreads();
-        load_tile(t);
+        store_tile();
         __syncthreads();
+        if (t + 1 < ntiles) fetch_tile(t + 1);
         const floatx16 acc = tile_logits();
         float part[RPW];
 #pragma unroll
@@ -334,7 +413,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int slot = (i >> 2) * 8 + half * 4 + (i & 3);
-            const float e = exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
+            const float e = __builtin_amdgcn_exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
             part[slot / CP] += e;
         }
         const int64_t j = t * kScoreTile + col;
@@ -656,7 +735,7 @@ hipError_t launch_checked(F&& f) {
 }  // namespace
 
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, hipStream_t s) {
+                            float* kbar, uint16_t* kbar3, hipStream_t s) {
     const int64_t chunks = BH * (N / kKvBlock) * (d / 4);
     const int threads = 256;
     const int64_t blocks = (chunks + threads - 1) / threads;
@@ -664,10 +743,10 @@ hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int 
     return launch_checked([&] {
         if (dt == kBF16)
             hipLaunchKernelGGL(mean_keys_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const uint16_t*>(k), kbar, chunks, d);
+                               static_cast<const uint16_t*>(k), kbar, kbar3, chunks, d);
         else
             hipLaunchKernelGGL(mean_keys_kernel<float>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const float*>(k), kbar, chunks, d);
+                               static_cast<const float*>(k), kbar, kbar3, chunks, d);
     });
 }
 
@@ -697,7 +776,7 @@ hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d, 
 }
 
 template <int CP>
-static void launch_scores_cp(const float* cent, const float* w, const float* kbar, int64_t BH,
+static void launch_scores_cp(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
                              int64_t QB, int64_t M, int d, int C, float* scores,
                              hipStream_t s) {
     constexpr int rows_per_wg = kScoreWaves * (32 / CP);
@@ -705,21 +784,21 @@ static void launch_scores_cp(const float* cent, const float* w, const float* kba
                     static_cast<unsigned>(BH));
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(d));
     if (d == 128)
-        hipLaunchKernelGGL((scores_kernel<CP, 128>), grid, dim3(256), 0, s, cent, w, kbar, QB, M,
+        hipLaunchKernelGGL((scores_kernel<CP, 128>), grid, dim3(256), 0, s, cent, w, kbar3, QB, M,
                            C, scale_log2, scores);
     else
-        hipLaunchKernelGGL((scores_kernel<CP, 64>), grid, dim3(256), 0, s, cent, w, kbar, QB, M,
+        hipLaunchKernelGGL((scores_kernel<CP, 64>), grid, dim3(256), 0, s, cent, w, kbar3, QB, M,
                            C, scale_log2, scores);
 }
 
-hipError_t launch_scores(const float* cent, const float* w, const float* kbar, int64_t BH,
+hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
                          int64_t QB, int64_t M, int d, int C, float* scores, hipStream_t s) {
     return launch_checked([&] {
-        if (C <= 1) launch_scores_cp<1>(cent, w, kbar, BH, QB, M, d, C, scores, s);
-        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar, BH, QB, M, d, C, scores, s);
-        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar, BH, QB, M, d, C, scores, s);
-        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar, BH, QB, M, d, C, scores, s);
-        else launch_scores_cp<16>(cent, w, kbar, BH, QB, M, d, C, scores, s);
+        if (C <= 1) launch_scores_cp<1>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
+        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
+        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
+        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
+        else launch_scores_cp<16>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
     });
 }
 
