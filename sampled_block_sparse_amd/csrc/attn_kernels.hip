@@ -31,8 +31,8 @@
 //   * Software pipeline with one barrier per tile: each wave issues tile
 //     t+1's S^T MFMAs next to tile t's softmax, then tile t's P V MFMAs. Two
 //     LDS buffers hold K and V of alternate tiles; K of tile t+2 is stored
-//     before the barrier and V after it, and the gather of tile t+3 into
-//     registers overlaps the next iteration. Two workgroups per CU. Block ids
+//     just before the barrier and V after it, and the gather of tile t+3
+//     into registers overlaps the whole next iteration. Two workgroups per CU. Block ids
 //     and log-weights come through scalar loads; gather addresses are 32-bit
 //     offsets from the head's base.
 //   * Softmax per 4-key group: the group max of the raw products sets the
@@ -435,18 +435,27 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
             }
             Snext = Sn;
             l_run = fmaf(l_run, st.alpha, st.psum);
-            // K of tile t+2 (unconditional: past the row's end it writes
-            // stale K that only the discarded S^T of the last tile reads)
-            store_k(buf);
+            // Keep the packed weights computed here, inside the interleaved
+            // phase: without this the compiler sinks them past the rescale
+            // branch below, next to their use.
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+                asm volatile("" : : "v"(pw[sl][0]), "v"(pw[sl][1]), "v"(pw[sl][2]), "v"(pw[sl][3]));
+            // The output is rescaled only in tiles where some lane's running
+            // max grew (alpha < 1 there; exactly 1 elsewhere).
+            if (__builtin_amdgcn_ballot_w64(st.alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) O[j][i] *= st.alpha;
+                }
+            }
             // Phase B: P V, one MFMA per chunk, V^T operands read two chunks
-            // ahead, and the rescale of the next output block by alpha spread
-            // over the current block's MFMAs.
+            // ahead.
             constexpr int PS = 4 * ND;
             uint4 va[PS];
             va[0] = v_operand(buf, 0, 0);
             va[1] = v_operand(buf, 0, 1);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) O[0][i] *= st.alpha;
 #pragma unroll
             for (int c = 0; c < PS; ++c) {
                 if (c + 2 < PS) va[c + 2] = v_operand(buf, (c + 2) / 4, (c + 2) % 4);
@@ -454,12 +463,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
                 O[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(va[c]), as_bf16x8(make_uint4(pw[sl][0], pw[sl][1], pw[sl][2], pw[sl][3])),
                     O[j], 0, 0, 0);
-                if (j + 1 < ND) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) O[j + 1][sl * 4 + e] *= st.alpha;
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // K of tile t+2, as late as the barrier allows (unconditional:
+            // past the row's end it writes stale K that only the discarded
+            // S^T of the last tile reads)
+            store_k(buf);
         }
         __syncthreads();
         // V of tile t+2 (past the row's end: stale data nobody reads)
