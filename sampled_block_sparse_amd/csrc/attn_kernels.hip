@@ -167,6 +167,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         cnt = P.rowptr[row + 1] - base;
     }
     const int64_t ntiles = (cnt + kTileBlocks - 1) / kTileBlocks;
+    const int cnt32 = static_cast<int>(cnt);              // <= M < 2^19
 
     // ---- the wave's queries as the B operand of S^T = K Q^T ----
     const int64_t my_q = q0 + wave * 32 + col;
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // Gather of one tile into registers; all K loads are issued before the V
     // loads, so that storing K waits only for the K half.
     auto load_tile = [&](int64_t t) {
+        const int t32 = static_cast<int>(t);
         uint32_t boff[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -225,14 +227,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int j = 0; j < BPP; ++j) {
                 const int tb = wave * 4 + p * BPP + j;
-                const int64_t gb = t * kTileBlocks + tb;
+                const int gb = t32 * kTileBlocks + tb;
                 if (DENSE) {
-                    blk_s[j] = static_cast<int>((gb < cnt) ? gb : (cnt - 1));
-                    lw_s[j] = (gb < cnt) ? 0.0f : -INFINITY;
+                    blk_s[j] = (gb < cnt32) ? gb : (cnt32 - 1);
+                    lw_s[j] = (gb < cnt32) ? 0.0f : -INFINITY;
                 } else {
                     blk_s[j] = __builtin_amdgcn_readlane(iv, tb);
                     const float lw = __int_as_float(__builtin_amdgcn_readlane(iv, 16 + tb));
-                    lw_s[j] = (gb < cnt) ? lw * kLog2e : -INFINITY;
+                    lw_s[j] = (gb < cnt32) ? lw * kLog2e : -INFINITY;
                 }
             }
             const int blk = (BPP == 1 || sub == 0) ? blk_s[0] : blk_s[BPP - 1];
@@ -342,19 +344,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // 0 on the first tile (m_run = -inf; a first tile always holds a valid
     // block, so its max is finite).
     constexpr int kSmItems = 8 + 1 + 32 + 16;
+    // The running max and the row sum are kept as 4 partials each (items
+    // rotate over them) so that their updates form short dependency chains.
+    // The row sum adds the bf16-rounded weights (one v_dot2 per packed pair
+    // against (1, 1)): numerator and normaliser then use the same weights.
     struct SmState {
         float lwv[2][4];
         float bias[2][4];
-        float mx, alpha, psum;
+        float mx[4], psum[4];
+        float alpha;
     };
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
     auto sm_item = [&](int it, SAcc& S, SmState& st, uint32_t (&pw)[4][4]) {
         if (it < 8) {
             const int kb = it >> 2, g = it & 3;
-            const float gm = fmaxf(fmaxf(S.v[kb][4 * g], S.v[kb][4 * g + 1]),
+            const float gm = fmaxf(__builtin_fmaxf(S.v[kb][4 * g], S.v[kb][4 * g + 1]) ,
                                    fmaxf(S.v[kb][4 * g + 2], S.v[kb][4 * g + 3]));
-            st.mx = fmaxf(st.mx, fmaf(gm, scale, st.lwv[kb][g]));
+            st.mx[it & 3] = fmaxf(st.mx[it & 3], fmaf(gm, scale, st.lwv[kb][g]));
         } else if (it == 8) {
-            const float mx = half_max(st.mx);
+            const float mx = half_max(fmaxf(fmaxf(st.mx[0], st.mx[1]), fmaxf(st.mx[2], st.mx[3])));
             const float m_new = fmaxf(m_run, mx);
             st.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
@@ -365,15 +374,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
             }
         } else if (it < 41) {
             const int e = it - 9, kb = e >> 4, i = e & 15;
-            const float pv = __builtin_amdgcn_exp2f(fmaf(S.v[kb][i], scale, st.bias[kb][i >> 2]));
-            S.v[kb][i] = pv;
-            st.psum += pv;
+            S.v[kb][i] = __builtin_amdgcn_exp2f(fmaf(S.v[kb][i], scale, st.bias[kb][i >> 2]));
         } else {
             // pw[slice][w] = bf16 pair (2w, 2w+1) of the 8 weights of 16-key
             // slice `slice` held by this lane
             const int k = it - 41, slice = k >> 2, w = k & 3;
             const int kb = slice >> 1, o = (slice & 1) * 8 + 2 * w;
             pw[slice][w] = pack_bf16x2(S.v[kb][o], S.v[kb][o + 1]);
+            st.psum[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, pw[slice][w]), ones2, st.psum[k & 3], false);
         }
     };
 
@@ -391,55 +400,66 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // Every wave runs the same instruction stream (a wave whose queries lie
     // past N computes on zero queries and stores nothing), which keeps the
     // loop free of branches around its loads and MFMAs.
-    SAcc Snext = qk(0);
+    SAcc Sa = qk(0);
     // every wave has read K of tile 0 before iteration 0 overwrites it
     __syncthreads();
-    for (int64_t t = 0; t < ntiles; ++t) {
+    // One pipeline step on tile t: Scur holds S^T of tile t, Snext receives
+    // S^T of tile t+1. The loop runs two steps per iteration with the roles
+    // of the two accumulator sets swapped, so no registers are copied.
+    auto step = [&](int64_t t, SAcc& Scur, SAcc& Snext) {
         const int buf = static_cast<int>(t & 1);
         {
             // Phase A: S^T of tile t+1 (from the other buffer; on the last
             // tile that is stale K and the result is never used), one MFMA
             // per chunk with its K operand read two chunks ahead, and the
             // softmax items of tile t spread over the chunks.
-            SAcc Scur = Snext;
             SmState st;
-            st.mx = -INFINITY;
-            st.psum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                st.mx[k] = -INFINITY;
+                st.psum[k] = 0.0f;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) st.lwv[kb][g] = lws[buf][kb * 8 + 2 * g + half];
             }
             constexpr int QS = 2 * NS;
+            // step i: key half i&1 (the two accumulator chains alternate),
+            // channel step i>>1
             auto kread = [&](int i) {
-                const int kb = i / NS, s2 = i % NS;
+                const int kb = i & 1, s2 = i >> 1;
                 return *reinterpret_cast<const uint4*>(
                     &Ks[buf ^ 1][(kb * 32 + col) * KS + s2 * 16 + half * 8]);
             };
             uint4 ka[QS];
             ka[0] = kread(0);
             ka[1] = kread(1);
-            SAcc Sn;
+            SAcc& Sn = Snext;
             Sn.v[0] = floatx16{};
             Sn.v[1] = floatx16{};
             uint32_t pw[4][4];
+            // Softmax items of phase A: the group maxima, the finalisation,
+            // and the exponentials and packs of keys 0..31 (accumulator kb=0);
+            // those of keys 32..63 go to phase B.
+            constexpr int kItemsA = 25 + 8, kItemsB = 16 + 8;
+            auto item_a = [](int ia) { return ia < 25 ? ia : 41 + (ia - 25); };
+            auto item_b = [](int ib) { return ib < 16 ? 25 + ib : 49 + (ib - 16); };
 #pragma unroll
             for (int c = 0; c < QS; ++c) {
                 if (c + 2 < QS) ka[c + 2] = kread(c + 2);
-                Sn.v[c / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(ka[c]), qb[c % NS], Sn.v[c / NS], 0, 0, 0);
+                Sn.v[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(ka[c]), qb[c >> 1], Sn.v[c & 1], 0, 0, 0);
 #pragma unroll
-                for (int it = c * kSmItems / QS; it < (c + 1) * kSmItems / QS; ++it)
-                    sm_item(it, Scur, st, pw);
+                for (int ia = c * kItemsA / QS; ia < (c + 1) * kItemsA / QS; ++ia)
+                    sm_item(item_a(ia), Scur, st, pw);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            Snext = Sn;
-            l_run = fmaf(l_run, st.alpha, st.psum);
-            // Keep the packed weights computed here, inside the interleaved
-            // phase: without this the compiler sinks them past the rescale
-            // branch below, next to their use.
+            // Keep the packed weights of keys 0..31 computed here, inside the
+            // interleaved phase: without this the compiler sinks them past
+            // the rescale branch below, next to their use.
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
+            for (int sl = 0; sl < 2; ++sl)
                 asm volatile("" : : "v"(pw[sl][0]), "v"(pw[sl][1]), "v"(pw[sl][2]), "v"(pw[sl][3]));
             // The output is rescaled only in tiles where some lane's running
             // max grew (alpha < 1 there; exactly 1 elsewhere).
@@ -450,21 +470,31 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
                     for (int i = 0; i < 16; ++i) O[j][i] *= st.alpha;
                 }
             }
-            // Phase B: P V, one MFMA per chunk, V^T operands read two chunks
-            // ahead.
+            // Phase B: P V, one MFMA per chunk with the V^T operands read two
+            // chunks ahead: first the two 16-key slices of keys 0..31 (for
+            // every output block) next to the softmax items of keys 32..63,
+            // then the slices of keys 32..63.
             constexpr int PS = 4 * ND;
+            constexpr int PHALF = 2 * ND;
+            auto pv_at = [](int c) { return c < PHALF ? (c / ND) : 2 + (c - PHALF) / ND; };
             uint4 va[PS];
-            va[0] = v_operand(buf, 0, 0);
-            va[1] = v_operand(buf, 0, 1);
+            va[0] = v_operand(buf, 0 % ND, pv_at(0));
+            va[1] = v_operand(buf, 1 % ND, pv_at(1));
 #pragma unroll
             for (int c = 0; c < PS; ++c) {
-                if (c + 2 < PS) va[c + 2] = v_operand(buf, (c + 2) / 4, (c + 2) % 4);
-                const int j = c / 4, sl = c % 4;
+                if (c + 2 < PS) va[c + 2] = v_operand(buf, (c + 2) % ND, pv_at(c + 2));
+                const int j = c % ND, sl = pv_at(c);
                 O[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(va[c]), as_bf16x8(make_uint4(pw[sl][0], pw[sl][1], pw[sl][2], pw[sl][3])),
                     O[j], 0, 0, 0);
+                if (c < PHALF) {
+#pragma unroll
+                    for (int ib = c * kItemsB / PHALF; ib < (c + 1) * kItemsB / PHALF; ++ib)
+                        sm_item(item_b(ib), Scur, st, pw);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            l_run = fmaf(l_run, st.alpha, (st.psum[0] + st.psum[1]) + (st.psum[2] + st.psum[3]));
             // K of tile t+2, as late as the barrier allows (unconditional:
             // past the row's end it writes stale K that only the discarded
             // S^T of the last tile reads)
@@ -475,6 +505,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         store_v(buf);
         if (t + 3 < ntiles) load_tile(t + 3);
         if (t + 4 < ntiles) load_plan(t + 4);
+    };
+    SAcc Sb;
+    for (int64_t t = 0; t < ntiles; t += 2) {
+        step(t, Sa, Sb);
+        if (t + 1 < ntiles) step(t + 1, Sb, Sa);
     }
 
     const float l_tot = half_sum(l_run);
