@@ -80,6 +80,7 @@ def get_lib():
                                          _i64, _vp]),
         "absa_dense_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp]),
         "absa_plan_destroy": (None, [_vp]),
+        "absa_release_cached_memory": (_i32, []),
         "absa_status_string": (ctypes.c_char_p, [_i32]),
         "absa_last_error": (ctypes.c_char_p, []),
     }
@@ -276,3 +277,9 @@ def absa_dense_attention(q, k, v, out=None, stream=None):
                                           _dev(out, "out"), _dtype_code(q), B, H, N, d,
                                           _stream(stream)))
     return out
+
+
+def absa_release_cached_memory():
+    """Return the library's cached plan memory on the current device to the
+    system (waits for the device)."""
+    _check(get_lib().absa_release_cached_memory())

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -21,6 +22,7 @@ using namespace absa;
 struct absa_plan_s {
     int64_t B = 0, H = 0, N = 0, d = 0, M = 0, QB = 0, rows = 0, nnz = 0;
     int32_t n_clusters = 0;
+    int device = 0;              // device whose memory pool holds the buffers
     int64_t* rowptr = nullptr;   // device [rows+1]
     int32_t* idx = nullptr;      // device [nnz]
     float* logw = nullptr;       // device [nnz]
@@ -65,11 +67,69 @@ bool inject_alloc_failure() {
     return v && std::strcmp(v, "alloc") == 0;
 }
 
-// Device buffers owned until release() hands them over.
+// Stream-ordered device memory. Plan buffers and plan-building temporaries
+// come from one library-owned pool per device that keeps freed memory for
+// reuse (unlimited release threshold): once the pool has grown to the largest
+// plan, building and destroying plans costs no driver allocation, unmapping
+// or device-wide synchronisation. absa_release_cached_memory() trims it.
+std::mutex g_pool_mutex;
+std::vector<hipMemPool_t> g_pools;
+
+hipError_t device_pool(int dev, bool create, hipMemPool_t* out) {
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    *out = nullptr;
+    if (dev < 0) return hipErrorInvalidDevice;
+    if (static_cast<size_t>(dev) >= g_pools.size()) g_pools.resize(dev + 1, nullptr);
+    if (!g_pools[dev] && create) {
+        hipMemPoolProps props;
+        std::memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        hipError_t e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep_all = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep_all);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        g_pools[dev] = pool;
+    }
+    *out = g_pools[dev];
+    return hipSuccess;
+}
+
+// Allocate from the current device's pool, ordered on stream s. On an
+// out-of-memory error the pool's cached memory is returned to the system
+// once and the allocation retried.
+hipError_t pool_alloc(void** p, size_t bytes, hipStream_t s) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipMemPool_t pool = nullptr;
+    e = device_pool(dev, true, &pool);
+    if (e != hipSuccess) return e;
+    e = hipMallocFromPoolAsync(p, bytes, pool, s);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) {
+        (void)hipGetLastError();
+        if (hipStreamSynchronize(s) == hipSuccess && hipMemPoolTrimTo(pool, 0) == hipSuccess)
+            e = hipMallocFromPoolAsync(p, bytes, pool, s);
+    }
+    return e;
+}
+
+// Device buffers owned until release() hands them over; whatever is left is
+// returned to the pool in the order of stream s.
 struct DeviceArena {
+    hipStream_t stream;
     std::vector<void*> ptrs;
+    explicit DeviceArena(hipStream_t s) : stream(s) {}
     ~DeviceArena() {
-        for (void* p : ptrs) (void)hipFree(p);
+        for (void* p : ptrs)
+            if (p) (void)hipFreeAsync(p, stream);
     }
     template <typename T>
     absa_status alloc(T** out, int64_t count, const char* what) {
@@ -78,7 +138,7 @@ struct DeviceArena {
         if (inject_alloc_failure())
             return fail(ABSA_ERR_OUT_OF_MEMORY, "%s: allocation failure injected", what);
         void* p = nullptr;
-        hipError_t e = hipMalloc(&p, static_cast<size_t>(count) * sizeof(T));
+        hipError_t e = pool_alloc(&p, static_cast<size_t>(count) * sizeof(T), stream);
         if (e != hipSuccess) return hip_fail(e, what);
         ptrs.push_back(p);
         *out = static_cast<T*>(p);
@@ -179,12 +239,24 @@ void keep(DeviceArena& arena, absa_plan_s* P) {
     arena.release(P->scores);
 }
 
+// Waits for the plan's device to go idle, then returns the plan's buffers to
+// that device's pool.
 void free_plan(absa_plan_s* P) {
     if (!P) return;
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    if (!have_cur || cur != P->device) (void)hipSetDevice(P->device);
+    (void)hipDeviceSynchronize();
     void* bufs[] = {P->rowptr, P->idx, P->logw, P->p, P->kbar, P->cent, P->w, P->scores};
     for (void* b : bufs)
-        if (b) (void)hipFree(b);
+        if (b) (void)hipFreeAsync(b, nullptr);
+    if (have_cur && cur != P->device) (void)hipSetDevice(cur);
     delete P;
+}
+
+absa_status set_plan_device(absa_plan_s* P) {
+    ABSA_HIP(hipGetDevice(&P->device), "current device");
+    return ABSA_OK;
 }
 
 }  // namespace
@@ -237,7 +309,8 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     const Dtype dt = (dtype == ABSA_BF16) ? kBF16 : kF32;
 
     absa_status st = [&]() -> absa_status {
-        DeviceArena arena;
+        ABSA_TRY(set_plan_device(P));
+        DeviceArena arena(s);
         uint16_t* kbar3 = nullptr;
         ABSA_TRY(arena.alloc(&P->kbar, B * H * M * d, "mean keys"));
         ABSA_TRY(arena.alloc(&kbar3, B * H * M * 3 * d, "split mean keys"));
@@ -255,11 +328,10 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
         ABSA_TRY(run_sip(P, P->scores, params->budget_blocks, params->seed, s, arena));
         keep(arena, P);
         if (!params->keep_intermediates) {
-            // the stream is idle after run_sip's final synchronisation
-            (void)hipFree(P->kbar); P->kbar = nullptr;
-            (void)hipFree(P->cent); P->cent = nullptr;
-            (void)hipFree(P->w); P->w = nullptr;
-            (void)hipFree(P->scores); P->scores = nullptr;
+            float* tmp[] = {P->kbar, P->cent, P->w, P->scores};
+            for (float* b : tmp)
+                if (b) (void)hipFreeAsync(b, s);
+            P->kbar = P->cent = P->w = P->scores = nullptr;
         }
         return ABSA_OK;
     }();
@@ -289,7 +361,8 @@ absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
     if (!P) return fail(ABSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
     fill_dims(P, B, H, N, d);
     absa_status st = [&]() -> absa_status {
-        DeviceArena arena;
+        ABSA_TRY(set_plan_device(P));
+        DeviceArena arena(s);
         ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, s, arena));
         keep(arena, P);
         return ABSA_OK;
@@ -339,7 +412,8 @@ absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx, const fl
     *P = tmp;
     P->nnz = nnz;
     absa_status st = [&]() -> absa_status {
-        DeviceArena arena;
+        ABSA_TRY(set_plan_device(P));
+        DeviceArena arena(s);
         ABSA_TRY(arena.alloc(&P->rowptr, P->rows + 1, "row pointers"));
         ABSA_TRY(arena.alloc(&P->idx, nnz, "plan indices"));
         ABSA_TRY(arena.alloc(&P->logw, nnz, "plan log-weights"));
@@ -464,6 +538,17 @@ absa_status absa_dense_attention(const void* q, const void* k, const void* v, vo
 void absa_plan_destroy(absa_plan plan) {
     if (!plan) return;
     free_plan(plan);
+}
+
+absa_status absa_release_cached_memory(void) {
+    int dev = 0;
+    ABSA_HIP(hipGetDevice(&dev), "current device");
+    hipMemPool_t pool = nullptr;
+    ABSA_HIP(device_pool(dev, false, &pool), "library memory pool");
+    if (!pool) return ABSA_OK;
+    ABSA_HIP(hipDeviceSynchronize(), "device synchronisation");
+    ABSA_HIP(hipMemPoolTrimTo(pool, 0), "trim the library memory pool");
+    return ABSA_OK;
 }
 
 const char* absa_status_string(absa_status status) {

@@ -201,6 +201,42 @@ def test_determinism():
     assert torch.equal(o1, o2)
 
 
+def test_pool_reuse_and_release():
+    """Plans built from recycled pool memory (after destroys, after a release
+    of the cache, interleaved with a live plan of another shape) equal a plan
+    built first."""
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=2, N=4096, d=128, seed=12))
+    qs, ks, vs = (x.to(DEV) for x in _inputs(B=1, H=1, N=1000, d=64, seed=13))
+    ref_plan = absa.absa_plan_create(q, k, 100, 5, keep_intermediates=True)
+    ref = ref_plan.export()
+    ref_scores = ref_plan.export_intermediate(absa.INTER_SCORES, 0, 64 * 1024)
+    ref_out = absa.absa_sparse_attention(ref_plan, q, k, v)
+    ref_plan.destroy()
+    small = absa.absa_plan_create(qs, ks, 20, 1)            # live across the rest
+    small_ref = small.export()
+    for release in (False, True, False):
+        if release:
+            absa.absa_release_cached_memory()
+        plan = absa.absa_plan_create(q, k, 100, 5, keep_intermediates=True)
+        got = plan.export()
+        for key in ref:
+            assert np.array_equal(ref[key], got[key]), key
+        assert np.array_equal(plan.export_intermediate(absa.INTER_SCORES, 0, 64 * 1024),
+                              ref_scores)
+        out = absa.absa_sparse_attention(plan, q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        plan.destroy()
+    got = small.export()
+    for key in small_ref:
+        assert np.array_equal(small_ref[key], got[key]), key
+    out_s = absa.absa_sparse_attention(small, qs, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_s.float()).all()
+    small.destroy()
+    absa.absa_release_cached_memory()
+
+
 def test_plan_mismatch_and_bad_scores():
     q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=64, seed=9))
     plan = absa.absa_plan_create(q, k, 10, 1)
