@@ -317,13 +317,15 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
         ABSA_TRY(arena.alloc(&P->cent, P->rows * C * d, "centroids"));
         ABSA_TRY(arena.alloc(&P->w, P->rows * C, "cluster weights"));
         ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
+        float2* part = nullptr;
+        ABSA_TRY(arena.alloc(&part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
         ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), P->kbar, kbar3, s),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
                                P->cent, P->w, s),
                  "k-means kernel");
         ABSA_HIP(launch_scores(P->cent, P->w, kbar3, B * H, P->QB, M, static_cast<int>(d), C,
-                               P->scores, s),
+                               part, P->scores, s),
                  "score kernel");
         ABSA_TRY(run_sip(P, P->scores, params->budget_blocks, params->seed, s, arena));
         keep(arena, P);

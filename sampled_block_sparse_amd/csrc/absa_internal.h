@@ -42,9 +42,13 @@ hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int 
 hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
                          int C, int iters, float* cent, float* w, hipStream_t s);
 
+// Number of float2 chunk statistics the score passes need (the part
+// argument of launch_scores).
+int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C);
+
 hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3,
                          int64_t BH, int64_t QB, int64_t M, int d, int C,
-                         float* scores, hipStream_t s);
+                         float2* part, float* scores, hipStream_t s);
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
                             int64_t M, int64_t budget, uint64_t seed, uint64_t* capmask,

@@ -258,19 +258,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTile = 32;
 
-template <int CP, int D>
+// The score contraction of one head runs in two passes over key chunks, so
+// the grid has (query-block groups) x (heads) x (chunks) workgroups and
+// fills the chip whatever the head count. Pass 1 (PASS2 = false) writes, per centroid and chunk, the running
+// max and sum of the centroid's exponentials over the chunk's keys; pass 2
+// combines a centroid's chunk statistics in chunk order (deterministic),
+// then recomputes the chunk's logits and writes the weighted sums.
+template <int CP, int D, bool PASS2>
 __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict__ cent,
                                                         const float* __restrict__ w,
                                                         const uint16_t* __restrict__ kbar3,
                                                         int64_t QB, int64_t M, int C,
+                                                        int chunk_tiles, int nchunks,
                                                         float scale_log2,
+                                                        float2* __restrict__ part,
                                                         float* __restrict__ scores) {
     constexpr int RPW = 32 / CP;                    // query blocks per wave
     constexpr int NSTEP = D / 16;                   // MFMA k-steps
     constexpr int KROW = 3 * D + 8;                 // LDS key row (bf16), padded
-    constexpr int CHUNKS = kScoreTile * 3 * D / 8;  // 16-byte chunks per tile
+    constexpr int CHUNKS = kScoreTile * 3 * D / 8;  // 16-byte pieces per tile
     constexpr int CPT = CHUNKS / 256;               // per thread
-    __shared__ __align__(16) uint16_t ks[kScoreTile * KROW];
+    __shared__ __align__(16) uint16_t ks[2][kScoreTile * KROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -279,6 +287,10 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     const int half = lane >> 5;
     const int64_t bh = blockIdx.y;
     const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * kScoreWaves + wave) * RPW;
+    const int chunk = blockIdx.z;
+    const int64_t ntiles = (M + kScoreTile - 1) / kScoreTile;
+    const int64_t t0 = static_cast<int64_t>(chunk) * chunk_tiles;
+    const int64_t t1 = (t0 + chunk_tiles < ntiles) ? t0 + chunk_tiles : ntiles;
 
     // A operands: this lane's centroid slot (row col of the 32x32 block),
     // channels s*16 + half*8 .. +8 of each step, in three bf16 planes.
@@ -308,40 +320,55 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         }
     }
 
-    const uint16_t* kb = kbar3 + bh * M * 3 * D;
-    const int64_t ntiles = (M + kScoreTile - 1) / kScoreTile;
-    uint4 pre[CPT];
+    // Accumulator row i of this lane is centroid slot (i/4)*8 + half*4 + i%4.
+    auto slot_of = [&](int i) { return (i >> 2) * 8 + half * 4 + (i & 3); };
+    auto slot_valid = [&](int slot) {
+        return (r0 + slot / CP < QB) && (slot % CP < C);
+    };
+    auto part_index = [&](int slot) {
+        return ((bh * QB + r0 + slot / CP) * C + slot % CP) * nchunks;
+    };
 
-    auto fetch_tile = [&](int64_t t) {
+    const uint16_t* kb = kbar3 + bh * M * 3 * D;
+    // Native vectors (not uint4 structs): their copies stay in registers.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 pre[CPT];
+    // Tile loads are unconditional: a key index past M is clamped to M-1 and
+    // its logits are never used, so the loop carries no divergent load.
+    auto fetch_tile = [&](int64_t t) __attribute__((always_inline)) {
         const int64_t j0 = t * kScoreTile;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int e = tid + 256 * i;
             const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
-            pre[i] = (j0 + key < M)
-                ? *reinterpret_cast<const uint4*>(kb + (j0 + key) * 3 * D + c8 * 8)
-                : make_uint4(0, 0, 0, 0);
+            const int64_t j = (j0 + key < M) ? j0 + key : M - 1;
+            pre[i] = *reinterpret_cast<const u32x4*>(kb + j * 3 * D + c8 * 8);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int e = tid + 256 * i;
             const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
-            *reinterpret_cast<uint4*>(&ks[key * KROW + c8 * 8]) = pre[i];
+            *reinterpret_cast<u32x4*>(&ks[buf][key * KROW + c8 * 8]) = pre[i];
         }
     };
     auto as8 = [](uint4 u) { return __builtin_bit_cast(bf16x8, u); };
-    auto tile_logits = [&]() {
-        floatx16 acc = {}, acc2 = {};
-        const uint16_t* kr = &ks[col * KROW + half * 8];
+    auto tile_logits = [&](int buf) __attribute__((always_inline)) {
+        floatx16 acc, acc2;
+        const uint16_t* kr = &ks[buf][col * KROW + half * 8];
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const bf16x8 b1 = as8(*reinterpret_cast<const uint4*>(kr + st * 16));
             const bf16x8 b2 = as8(*reinterpret_cast<const uint4*>(kr + D + st * 16));
             const bf16x8 b3 = as8(*reinterpret_cast<const uint4*>(kr + 2 * D + st * 16));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, acc, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, acc2, 0, 0, 0);
+            if (st == 0) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, floatx16{}, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, floatx16{}, 0, 0, 0);
+            } else {
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, acc, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, acc2, 0, 0, 0);
+            }
             acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b2, acc2, 0, 0, 0);
             acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b3, acc2, 0, 0, 0);
             acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b1, acc2, 0, 0, 0);
@@ -351,90 +378,117 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         for (int i = 0; i < 16; ++i) acc[i] += acc2[i];
         return acc;
     };
+    // Double-buffered key tiles, one barrier per tile: tile t is read from
+    // buffer (t - t0) & 1 while tile t+1 is stored into the other buffer
+    // (last read before the previous barrier) and tile t+2 is loaded.
+    auto for_tiles = [&](auto&& body) __attribute__((always_inline)) {
+        fetch_tile(t0);
+        store_tile(0);
+        fetch_tile((t0 + 1 < t1) ? t0 + 1 : t0);
+        __syncthreads();
+        for (int64_t t = t0; t < t1; ++t) {
+            const int buf = static_cast<int>((t - t0) & 1);
+            const floatx16 acc = tile_logits(buf);
+            store_tile(buf ^ 1);
+            fetch_tile((t + 2 < t1) ? t + 2 : t1 - 1);
+            body(t, acc);
+            __syncthreads();
+        }
+    };
 
-    // Pass 1: running max and sum per centroid row held by this lane.
-    float mx[16], zs[16];
+    if constexpr (!PASS2) {
+        // Running max and sum per centroid row held by this lane; one
+        // exponential per logit: exp2(-|x - max|) either scales the old sum
+        // (new max) or is the new term.
+        float mx[16], zs[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { mx[i] = -INFINITY; zs[i] = 0.0f; }
-    fetch_tile(0);
-    for (int64_t t = 0; t < ntiles; ++t) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t + 1 < ntiles) fetch_tile(t + 1);
-        const floatx16 acc = tile_logits();
-        if (t * kScoreTile + col < M) {
+        for (int i = 0; i < 16; ++i) { mx[i] = -INFINITY; zs[i] = 0.0f; }
+        for_tiles([&](int64_t t, floatx16 acc) __attribute__((always_inline)) {
+            if (t * kScoreTile + col < M) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float x = acc[i] * scale_log2;
+                    const float dd = x - mx[i];
+                    const float e = __builtin_amdgcn_exp2f(-fabsf(dd));
+                    const bool up = dd > 0.0f;
+                    zs[i] = up ? fmaf(zs[i], e, 1.0f) : zs[i] + e;
+                    mx[i] = up ? x : mx[i];
+                }
+            }
+        });
+        // Merge the 32 columns of each half (xor over lane bits 0..4).
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float x = acc[i] * scale_log2;
-                const float mn = fmaxf(mx[i], x);
-                zs[i] = zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn) + __builtin_amdgcn_exp2f(x - mn);
+                const float m2 = __shfl_xor(mx[i], off);
+                const float z2 = __shfl_xor(zs[i], off);
+                const float mn = fmaxf(mx[i], m2);
+                const float e1 =
+                    (mx[i] == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn);
+                const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * __builtin_amdgcn_exp2f(m2 - mn);
+                zs[i] = e1 + e2;
                 mx[i] = mn;
             }
         }
-    }
-    // Merge the 32 columns of each half (xor over lane bits 0..4).
+        if (col == 0) {
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float m2 = __shfl_xor(mx[i], off);
-            const float z2 = __shfl_xor(zs[i], off);
-            const float mn = fmaxf(mx[i], m2);
-            const float e1 = (mx[i] == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn);
-            const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * __builtin_amdgcn_exp2f(m2 - mn);
-            zs[i] = e1 + e2;
-            mx[i] = mn;
-        }
-    }
-    // Coefficient w_m / Z_m of every row this lane holds.
-    float coef[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int slot = (i >> 2) * 8 + half * 4 + (i & 3);
-        const int64_t rr = r0 + slot / CP;
-        const int mm = slot % CP;
-        const bool ok = (rr < QB) && (mm < C);
-        coef[i] = ok ? w[(bh * QB + rr) * C + mm] / zs[i] : 0.0f;
-        if (!ok) mx[i] = 0.0f;
-    }
-
-    // Pass 2: weighted sum over each query block's clusters.
-    fetch_tile(0);
-    for (int64_t t = 0; t < ntiles; ++t) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t + 1 < ntiles) fetch_tile(t + 1);
-        const floatx16 acc = tile_logits();
-        float part[RPW];
-#pragma unroll
-        for (int g = 0; g < RPW; ++g) part[g] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int slot = (i >> 2) * 8 + half * 4 + (i & 3);
-            const float e = __builtin_amdgcn_exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
-            part[slot / CP] += e;
-        }
-        const int64_t j = t * kScoreTile + col;
-        if (CP >= 8) {
-            // A query block's clusters span both halves: add the partner's.
-#pragma unroll
-            for (int g = 0; g < RPW; ++g) part[g] += __shfl_xor(part[g], 32);
-#pragma unroll
-            for (int g = 0; g < RPW; ++g) {
-                const int64_t rr = r0 + g;
-                if ((g & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = part[g];
-            }
-        } else {
-#pragma unroll
-            for (int g = 0; g < RPW; ++g) {
-                // rows g with bit (CP's half bit) matching this half
-                const int half_of_g = ((g * CP) >> 2) & 1;
-                const int64_t rr = r0 + g;
-                if (half_of_g == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = part[g];
+            for (int i = 0; i < 16; ++i) {
+                const int slot = slot_of(i);
+                if (slot_valid(slot)) part[part_index(slot) + chunk] = make_float2(mx[i], zs[i]);
             }
         }
+    } else {
+        // Max and sum of each centroid over all chunks, in chunk order, and
+        // the coefficient w_m / Z_m of every row this lane holds.
+        float mx[16], coef[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int slot = slot_of(i);
+            mx[i] = 0.0f;
+            coef[i] = 0.0f;
+            if (slot_valid(slot)) {
+                const float2* pp = part + part_index(slot);
+                float m = -INFINITY;
+                for (int c = 0; c < nchunks; ++c) m = fmaxf(m, pp[c].x);
+                float z = 0.0f;
+                for (int c = 0; c < nchunks; ++c) {
+                    const float2 q = pp[c];
+                    if (q.x != -INFINITY) z += q.y * __builtin_amdgcn_exp2f(q.x - m);
+                }
+                mx[i] = m;
+                coef[i] = w[(bh * QB + r0 + slot / CP) * C + slot % CP] / z;
+            }
+        }
+        for_tiles([&](int64_t t, floatx16 acc) __attribute__((always_inline)) {
+            float pr[RPW];
+#pragma unroll
+            for (int g = 0; g < RPW; ++g) pr[g] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
+                pr[slot_of(i) / CP] += e;
+            }
+            const int64_t j = t * kScoreTile + col;
+            if (CP >= 8) {
+                // A query block's clusters span both halves: add the partner's.
+#pragma unroll
+                for (int g = 0; g < RPW; ++g) pr[g] += __shfl_xor(pr[g], 32);
+#pragma unroll
+                for (int g = 0; g < RPW; ++g) {
+                    const int64_t rr = r0 + g;
+                    if ((g & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[g];
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < RPW; ++g) {
+                    // rows g whose slots lie in this lane's half
+                    const int half_of_g = ((g * CP) >> 2) & 1;
+                    const int64_t rr = r0 + g;
+                    if (half_of_g == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[g];
+                }
+            }
+        });
     }
 }
 
@@ -775,30 +829,68 @@ hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d, 
     });
 }
 
+// Key chunking of the score passes: whole rows of keys when the
+// (query-block group x head) grid alone fills the chip, else just enough
+// even chunks for about kScoreMinGroups workgroups. Splitting costs a
+// second read of every chunk's statistics, so it is kept for small grids.
+constexpr int64_t kScoreMinGroups = 1024;
+
+static void score_chunks(int64_t groups, int64_t M, int* chunk_tiles, int* nchunks) {
+    const int64_t ntiles = (M + kScoreTile - 1) / kScoreTile;
+    int64_t n = (kScoreMinGroups + groups - 1) / groups;
+    if (n > ntiles) n = ntiles;
+    if (n < 1) n = 1;
+    *chunk_tiles = static_cast<int>((ntiles + n - 1) / n);
+    *nchunks = static_cast<int>((ntiles + *chunk_tiles - 1) / *chunk_tiles);
+}
+
+static int64_t score_groups(int64_t BH, int64_t QB, int C) {
+    const int cp = C <= 1 ? 1 : C <= 2 ? 2 : C <= 4 ? 4 : C <= 8 ? 8 : 16;
+    const int64_t rows_per_wg = kScoreWaves * (32 / cp);
+    return BH * ((QB + rows_per_wg - 1) / rows_per_wg);
+}
+
+int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C) {
+    int ct = 0, nc = 0;
+    score_chunks(score_groups(BH, QB, C), M, &ct, &nc);
+    return BH * QB * C * nc;
+}
+
+template <int CP, int D>
+static void launch_scores_cpd(const float* cent, const float* w, const uint16_t* kbar3,
+                              int64_t BH, int64_t QB, int64_t M, int C, float2* part,
+                              float* scores, hipStream_t s) {
+    constexpr int rows_per_wg = kScoreWaves * (32 / CP);
+    int chunk_tiles = 0, nchunks = 0;
+    score_chunks(score_groups(BH, QB, C), M, &chunk_tiles, &nchunks);
+    const dim3 grid(static_cast<unsigned>((QB + rows_per_wg - 1) / rows_per_wg),
+                    static_cast<unsigned>(BH), static_cast<unsigned>(nchunks));
+    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    hipLaunchKernelGGL((scores_kernel<CP, D, false>), grid, dim3(256), 0, s, cent, w, kbar3, QB,
+                       M, C, chunk_tiles, nchunks, scale_log2, part, scores);
+    hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kbar3, QB,
+                       M, C, chunk_tiles, nchunks, scale_log2, part, scores);
+}
+
 template <int CP>
 static void launch_scores_cp(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
-                             int64_t QB, int64_t M, int d, int C, float* scores,
+                             int64_t QB, int64_t M, int d, int C, float2* part, float* scores,
                              hipStream_t s) {
-    constexpr int rows_per_wg = kScoreWaves * (32 / CP);
-    const dim3 grid(static_cast<unsigned>((QB + rows_per_wg - 1) / rows_per_wg),
-                    static_cast<unsigned>(BH));
-    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(d));
     if (d == 128)
-        hipLaunchKernelGGL((scores_kernel<CP, 128>), grid, dim3(256), 0, s, cent, w, kbar3, QB, M,
-                           C, scale_log2, scores);
+        launch_scores_cpd<CP, 128>(cent, w, kbar3, BH, QB, M, C, part, scores, s);
     else
-        hipLaunchKernelGGL((scores_kernel<CP, 64>), grid, dim3(256), 0, s, cent, w, kbar3, QB, M,
-                           C, scale_log2, scores);
+        launch_scores_cpd<CP, 64>(cent, w, kbar3, BH, QB, M, C, part, scores, s);
 }
 
 hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
-                         int64_t QB, int64_t M, int d, int C, float* scores, hipStream_t s) {
+                         int64_t QB, int64_t M, int d, int C, float2* part, float* scores,
+                         hipStream_t s) {
     return launch_checked([&] {
-        if (C <= 1) launch_scores_cp<1>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
-        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
-        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
-        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
-        else launch_scores_cp<16>(cent, w, kbar3, BH, QB, M, d, C, scores, s);
+        if (C <= 1) launch_scores_cp<1>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
+        else launch_scores_cp<16>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
     });
 }
 
