@@ -192,20 +192,18 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
                     hipStream_t s, DeviceArena& arena) {
     const int64_t rows = P->rows;
     const int64_t words = (P->M + 63) / 64;
-    uint64_t* capmask = nullptr;
     uint64_t* keepmask = nullptr;
     SipRow* rowinfo = nullptr;
     int64_t* counts = nullptr;
     PlanStatus* status = nullptr;
-    ABSA_TRY(arena.alloc(&capmask, rows * words, "cap mask"));
     ABSA_TRY(arena.alloc(&keepmask, rows * words, "keep mask"));
     ABSA_TRY(arena.alloc(&rowinfo, rows, "row info"));
     ABSA_TRY(arena.alloc(&counts, rows, "row counts"));
     ABSA_TRY(arena.alloc(&status, 1, "plan status"));
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
     ABSA_HIP(hipMemsetAsync(status, 0, sizeof(PlanStatus), s), "clear plan status");
-    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, capmask, keepmask,
-                              rowinfo, counts, status, s),
+    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, keepmask, rowinfo,
+                              counts, status, s),
              "SIP count kernel");
     ABSA_HIP(launch_scan(counts, rows, P->rowptr, status, s), "row scan kernel");
     PlanStatus host{};
@@ -220,7 +218,7 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
     ABSA_TRY(arena.alloc(&P->logw, P->nnz, "plan log-weights"));
     ABSA_TRY(arena.alloc(&P->p, P->nnz, "plan probabilities"));
     if (P->nnz > 0) {
-        ABSA_HIP(launch_sip_fill(scores, rows, P->M, capmask, keepmask, rowinfo, P->rowptr,
+        ABSA_HIP(launch_sip_fill(scores, rows, P->M, keepmask, rowinfo, P->rowptr,
                                  P->idx, P->logw, P->p, s),
                  "SIP fill kernel");
     }

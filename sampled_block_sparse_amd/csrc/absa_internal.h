@@ -18,12 +18,12 @@ enum Dtype : int { kBF16 = 0, kF32 = 1 };
 //   mode 0: every still-active block has p = 1
 //   mode 1: every still-active block has p = left / n_active (all scores 0)
 //   mode 2: every still-active block has p = c * q_j
-// Capped blocks carry a set bit in the row's cap mask, kept blocks in its
-// keep mask.
+// The capped blocks (p = 1) are exactly those with score >= thr (+inf when
+// no block is capped).
 struct SipRow {
     double c;          // mode 2 multiplier, or left/n_active for mode 1
     int32_t mode;
-    int32_t pad;
+    float thr;
 };
 
 // Device-side status written at the end of the SIP count + scan and read
@@ -51,17 +51,17 @@ hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar
                          float2* part, float* scores, hipStream_t s);
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
-                            int64_t M, int64_t budget, uint64_t seed, uint64_t* capmask,
-                            uint64_t* keepmask, SipRow* rowinfo, int64_t* counts,
-                            PlanStatus* status, hipStream_t s);
+                            int64_t M, int64_t budget, uint64_t seed, uint64_t* keepmask,
+                            SipRow* rowinfo, int64_t* counts, PlanStatus* status,
+                            hipStream_t s);
 
 hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr,
                        PlanStatus* status, hipStream_t s);
 
 hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
-                           const uint64_t* capmask, const uint64_t* keepmask,
-                           const SipRow* rowinfo, const int64_t* rowptr, int32_t* idx,
-                           float* logw, double* p, hipStream_t s);
+                           const uint64_t* keepmask, const SipRow* rowinfo,
+                           const int64_t* rowptr, int32_t* idx, float* logw, double* p,
+                           hipStream_t s);
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, void* o,
                             Dtype dt, int64_t B, int64_t H, int64_t N, int d,

@@ -521,8 +521,10 @@ __device__ __forceinline__ void philox_10(uint32_t c[4], uint32_t k0, uint32_t k
     constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
     for (int rnd = 0; rnd < 10; ++rnd) {
-        const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
-        const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
+        const uint64_t p0 = static_cast<uint64_t>(M0) * c[0];
+        const uint64_t p1 = static_cast<uint64_t>(M1) * c[2];
+        const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+        const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
         const uint32_t n0 = hi1 ^ c[1] ^ k0;
         const uint32_t n2 = hi0 ^ c[3] ^ k1;
         c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
@@ -555,15 +557,46 @@ __device__ __forceinline__ double sip_p(bool capped, const SipRow& ri, float s) 
     return ri.c * fixed_point(s);
 }
 
+// Smallest integer T >= 1 with fl(c * T) >= 1 for the IEEE double product,
+// capped at 2^53. fl(c * q) is non-decreasing in q, so for an integer q,
+// fl(c * q) >= 1 exactly when q >= T. ceil(fl(1 / c)) lies within two of T,
+// so a few exact integer steps in double find it.
+__device__ __forceinline__ double cap_threshold(double c) {
+    double t = ceil(1.0 / c);
+    if (!(t < 0x1.0p53)) t = 0x1.0p53;
+    if (t < 1.0) t = 1.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (t > 1.0 && c * (t - 1.0) >= 1.0) t -= 1.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (t < 0x1.0p53 && c * t < 1.0) t += 1.0;
+    return t;
+}
+
+// Smallest fp32 value s with s >= x (x > 0 and finite). For an fp32 score s
+// and an integer T, floor(s * 2^52) >= T exactly when s >= this of T * 2^-52.
+__device__ __forceinline__ float fp32_at_least(double x) {
+    float f = static_cast<float>(x);
+    if (static_cast<double>(f) < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+    return f;
+}
+
 // ---------------------------------------------------------------------------
 // SIP probabilities and draws [hamidun, SIP paragraph; edumints, SIP item]:
 // capped water-filling in exact fixed point (q_j = floor(s_j 2^52), exact
 // sums, IEEE double division and product), then one Poisson draw per block.
-// One workgroup per plan row. With LDS_ROW the row's scores live in LDS and a
-// capped block is marked by negating its score; otherwise the scores are
-// re-read from global memory and caps kept in the global cap mask. The
-// kernel writes the row's cap and keep masks (one bit per block), its count
-// and the final multiplier.
+// One workgroup per plan row; with LDS_ROW the row's scores are staged in
+// LDS, otherwise every pass re-reads them from global memory.
+//
+// A round of the water-filling caps the still-active blocks with
+// fl(c q_j) >= 1, i.e. q_j >= T(c) (cap_threshold), i.e. s_j >= thr(c) for
+// the fp32 threshold fp32_at_least(T 2^-52). The capped set after any round
+// is therefore {s_j >= thr_min}, thr_min the smallest threshold of a round
+// that capped something, and a round's new caps are the blocks with
+// thr <= s_j < thr_min: one fp32 comparison per block and round, and no
+// per-block cap state. The row's outcome (mode, c, thr_min) goes to rowinfo,
+// its keep mask (one bit per block, from the Philox draws) to keepmask.
 // ---------------------------------------------------------------------------
 constexpr int kSipThreads = 512;
 constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
@@ -571,18 +604,18 @@ constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
 template <bool LDS_ROW>
 __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
-    uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
-    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    uint64_t seed, uint64_t* __restrict__ keepmask, SipRow* __restrict__ rowinfo,
+    int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     extern __shared__ float sv[];
     __shared__ double redd[kSipThreads / 64];
     __shared__ int redi[kSipThreads / 64];
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
-    uint64_t* cm = capmask + row * words;
     uint64_t* km = keepmask + row * words;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    auto score = [&](int64_t j) { return LDS_ROW ? sv[j] : sg[j]; };
 
     double sum = 0.0;
     int bad = 0;
@@ -592,11 +625,6 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         else sum += fixed_point(v);
         if (LDS_ROW) sv[j] = v;
     }
-    if (!LDS_ROW) {
-        // each 64-block word is owned by the wave that later tests and sets it
-        for (int64_t base = 0; base < M; base += kSipThreads)
-            if (lane == 0 && base + wave * 64 < M) cm[(base >> 6) + wave] = 0;
-    }
     const double total = block_sum(sum, redd);
     const int nbad = block_sum(bad, redi);
     if (nbad != 0 || total >= 0x1.0p53) {
@@ -605,14 +633,15 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
             counts[row] = 0;
             rowinfo[row].mode = 0;
             rowinfo[row].c = 0.0;
+            rowinfo[row].thr = INFINITY;
         }
         return;
     }
 
     int64_t taken = 0, n_active = M;
     double S = total;
+    float thr_min = INFINITY;
     SipRow ri;
-    ri.pad = 0;
     for (;;) {
         const int64_t left = budget - taken;
         if (left >= n_active) { ri.mode = 0; ri.c = 1.0; break; }
@@ -622,33 +651,15 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
             break;
         }
         const double c = static_cast<double>(left) / S;
+        const float thr = fp32_at_least(cap_threshold(c) * 0x1.0p-52);
         int ncap = 0;
         double scap = 0.0;
-        for (int64_t base = 0; base < M; base += kSipThreads) {
-            const int64_t j = base + tid;
-            bool hit = false;
-            double dq = 0.0;
-            if (j < M) {
-                if (LDS_ROW) {
-                    const float v = sv[j];
-                    if (v >= 0.0f) {
-                        dq = fixed_point(v);
-                        hit = c * dq >= 1.0;
-                        if (hit) sv[j] = -v;
-                    }
-                } else {
-                    const bool was = (cm[j >> 6] >> (j & 63)) & 1ull;
-                    if (!was) {
-                        dq = fixed_point(sg[j]);
-                        hit = c * dq >= 1.0;
-                    }
-                }
+        for (int64_t j = tid; j < M; j += kSipThreads) {
+            const float v = score(j);
+            if (v >= thr && v < thr_min) {
+                ++ncap;
+                scap += fixed_point(v);
             }
-            if (!LDS_ROW) {
-                const uint64_t bal = __ballot(hit);
-                if (lane == 0 && bal) cm[j >> 6] |= bal;
-            }
-            if (hit) { ++ncap; scap += dq; }
         }
         const int tcap = block_sum(ncap, redi);
         const double tsum = block_sum(scap, redd);
@@ -656,7 +667,9 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         taken += tcap;
         n_active -= tcap;
         S -= tsum;
+        thr_min = fminf(thr_min, thr);
     }
+    ri.thr = thr_min;
 
     const int64_t bidx = row / QB;
     const int64_t r = row - bidx * QB;
@@ -665,25 +678,13 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     int kept = 0;
     for (int64_t base = 0; base < M; base += kSipThreads) {
         const int64_t j = base + tid;
-        bool keep = false, capped = false;
+        bool keep = false;
         if (j < M) {
-            float v;
-            if (LDS_ROW) {
-                v = sv[j];
-                capped = v < 0.0f;
-                v = fabsf(v);
-            } else {
-                capped = (cm[j >> 6] >> (j & 63)) & 1ull;
-                v = sg[j];
-            }
-            keep = sip_uniform(seed, b, h, r, j) < sip_p(capped, ri, v);
+            const float v = score(j);
+            keep = sip_uniform(seed, b, h, r, j) < sip_p(v >= thr_min, ri, v);
         }
         const uint64_t kb = __ballot(keep);
-        const uint64_t cb = __ballot(capped);
-        if (lane == 0 && base + wave * 64 < M) {
-            km[(base >> 6) + wave] = kb;
-            if (LDS_ROW) cm[(base >> 6) + wave] = cb;
-        }
+        if (lane == 0 && base + wave * 64 < M) km[(base >> 6) + wave] = kb;
         kept += keep ? 1 : 0;
     }
     const int tk = block_sum(kept, redi);
@@ -732,7 +733,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
 // a 256-word chunk; an exclusive scan of the words' popcounts gives each
 // thread the position of its first kept block.
 __global__ __launch_bounds__(256) void sip_fill_kernel(
-    const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
+    const float* __restrict__ scores, int64_t M,
     const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
     const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
     double* __restrict__ p_out) {
@@ -740,7 +741,6 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
-    const uint64_t* cm = capmask + row * words;
     const uint64_t* km = keepmask + row * words;
     const SipRow ri = rowinfo[row];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -748,7 +748,6 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     for (int64_t base = 0; base < words; base += 256) {
         const int64_t w = base + tid;
         const uint64_t kw = (w < words) ? km[w] : 0ull;
-        const uint64_t cw = (w < words) ? cm[w] : 0ull;
         const int pc = __popcll(kw);
         int incl = pc;
 #pragma unroll
@@ -769,7 +768,8 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
             const int bit = __ffsll(static_cast<long long>(bits)) - 1;
             bits &= bits - 1;
             const int64_t j = w * 64 + bit;
-            const double p = sip_p((cw >> bit) & 1ull, ri, sg[j]);
+            const float v = sg[j];
+            const double p = sip_p(v >= ri.thr, ri, v);
             idx[at] = static_cast<int32_t>(j);
             logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
             p_out[at] = p;
@@ -895,8 +895,8 @@ hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar
 }
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
-                            int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
-                            SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
+                            int64_t budget, uint64_t seed, uint64_t* keepmask, SipRow* rowinfo,
+                            int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
     if (M <= kSipLdsMaxBlocks) {
         const size_t shm = static_cast<size_t>(M) * sizeof(float);
@@ -906,13 +906,12 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
         if (e != hipSuccess) return e;
         return launch_checked([&] {
             hipLaunchKernelGGL(sip_count_kernel<true>, dim3(rows), dim3(kSipThreads), shm, s,
-                               scores, H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts,
-                               status);
+                               scores, H, QB, M, budget, seed, keepmask, rowinfo, counts, status);
         });
     }
     return launch_checked([&] {
         hipLaunchKernelGGL(sip_count_kernel<false>, dim3(rows), dim3(kSipThreads), 0, s, scores,
-                           H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts, status);
+                           H, QB, M, budget, seed, keepmask, rowinfo, counts, status);
     });
 }
 
@@ -923,12 +922,12 @@ hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr, Pla
     });
 }
 
-hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M, const uint64_t* capmask,
+hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
                            const uint64_t* keepmask, const SipRow* rowinfo, const int64_t* rowptr,
                            int32_t* idx, float* logw, double* p, hipStream_t s) {
     return launch_checked([&] {
-        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, capmask,
-                           keepmask, rowinfo, rowptr, idx, logw, p);
+        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, keepmask,
+                           rowinfo, rowptr, idx, logw, p);
     });
 }
 
