@@ -192,18 +192,20 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
                     hipStream_t s, DeviceArena& arena) {
     const int64_t rows = P->rows;
     const int64_t words = (P->M + 63) / 64;
+    uint64_t* capmask = nullptr;
     uint64_t* keepmask = nullptr;
     SipRow* rowinfo = nullptr;
     int64_t* counts = nullptr;
     PlanStatus* status = nullptr;
+    ABSA_TRY(arena.alloc(&capmask, rows * words, "cap mask"));
     ABSA_TRY(arena.alloc(&keepmask, rows * words, "keep mask"));
     ABSA_TRY(arena.alloc(&rowinfo, rows, "row info"));
     ABSA_TRY(arena.alloc(&counts, rows, "row counts"));
     ABSA_TRY(arena.alloc(&status, 1, "plan status"));
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
     ABSA_HIP(hipMemsetAsync(status, 0, sizeof(PlanStatus), s), "clear plan status");
-    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, keepmask, rowinfo,
-                              counts, status, s),
+    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, capmask, keepmask,
+                              rowinfo, counts, status, s),
              "SIP count kernel");
     ABSA_HIP(launch_scan(counts, rows, P->rowptr, status, s), "row scan kernel");
     PlanStatus host{};
@@ -218,7 +220,7 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
     ABSA_TRY(arena.alloc(&P->logw, P->nnz, "plan log-weights"));
     ABSA_TRY(arena.alloc(&P->p, P->nnz, "plan probabilities"));
     if (P->nnz > 0) {
-        ABSA_HIP(launch_sip_fill(scores, rows, P->M, keepmask, rowinfo, P->rowptr,
+        ABSA_HIP(launch_sip_fill(scores, rows, P->M, capmask, keepmask, rowinfo, P->rowptr,
                                  P->idx, P->logw, P->p, s),
                  "SIP fill kernel");
     }
@@ -507,6 +509,34 @@ static absa_status attention_common(const void* q, const void* k, const void* v,
     return check_shape(B, H, N, d);
 }
 
+// Launch the attention kernel on bf16 inputs. fp32 inputs are first rounded
+// to bf16 (round to nearest even) into temporaries from the library's pool,
+// ordered on the same stream; the output keeps the caller's dtype.
+static absa_status run_attention(const void* q, const void* k, const void* v, void* o,
+                                 absa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 const absa_plan_s* plan, hipStream_t s) {
+    const int64_t n = B * H * N * d;
+    const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
+                   *v16 = static_cast<const uint16_t*>(v);
+    DeviceArena arena(s);
+    if (dtype == ABSA_F32) {
+        uint16_t* tmp[3] = {nullptr, nullptr, nullptr};
+        const void* src[3] = {q, k, v};
+        for (int i = 0; i < 3; ++i) {
+            ABSA_TRY(arena.alloc(&tmp[i], n, "bf16 copy of an fp32 input"));
+            ABSA_HIP(launch_to_bf16(static_cast<const float*>(src[i]), tmp[i], n, s),
+                     "fp32 to bf16 kernel");
+        }
+        q16 = tmp[0]; k16 = tmp[1]; v16 = tmp[2];
+    }
+    const bool dense = (plan == nullptr);
+    ABSA_HIP(launch_attention(q16, k16, v16, o, dtype == ABSA_F32, B, H, N, static_cast<int>(d),
+                              dense ? nullptr : plan->rowptr, dense ? nullptr : plan->idx,
+                              dense ? nullptr : plan->logw, dense, s),
+             dense ? "dense attention kernel" : "sparse attention kernel");
+    return ABSA_OK;
+}
+
 absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k, const void* v,
                                   void* o, absa_dtype dtype, int64_t B, int64_t H, int64_t N,
                                   int64_t d, void* hip_stream) {
@@ -517,22 +547,15 @@ absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k, 
                     "plan built for (B,H,N,d) = (%lld,%lld,%lld,%lld), called with (%lld,%lld,%lld,%lld)",
                     (long long)plan->B, (long long)plan->H, (long long)plan->N, (long long)plan->d,
                     (long long)B, (long long)H, (long long)N, (long long)d);
-    ABSA_HIP(launch_attention(q, k, v, o, dtype == ABSA_BF16 ? kBF16 : kF32, B, H, N,
-                              static_cast<int>(d), plan->rowptr, plan->idx, plan->logw, false,
-                              static_cast<hipStream_t>(hip_stream)),
-             "sparse attention kernel");
-    return ABSA_OK;
+    return run_attention(q, k, v, o, dtype, B, H, N, d, plan, static_cast<hipStream_t>(hip_stream));
 }
 
 absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
                                  absa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
                                  void* hip_stream) {
     ABSA_TRY(attention_common(q, k, v, o, dtype, B, H, N, d));
-    ABSA_HIP(launch_attention(q, k, v, o, dtype == ABSA_BF16 ? kBF16 : kF32, B, H, N,
-                              static_cast<int>(d), nullptr, nullptr, nullptr, true,
-                              static_cast<hipStream_t>(hip_stream)),
-             "dense attention kernel");
-    return ABSA_OK;
+    return run_attention(q, k, v, o, dtype, B, H, N, d, nullptr,
+                         static_cast<hipStream_t>(hip_stream));
 }
 
 void absa_plan_destroy(absa_plan plan) {

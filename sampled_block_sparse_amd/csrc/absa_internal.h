@@ -51,20 +51,25 @@ hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar
                          float2* part, float* scores, hipStream_t s);
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
-                            int64_t M, int64_t budget, uint64_t seed, uint64_t* keepmask,
-                            SipRow* rowinfo, int64_t* counts, PlanStatus* status,
-                            hipStream_t s);
+                            int64_t M, int64_t budget, uint64_t seed, uint64_t* capmask,
+                            uint64_t* keepmask, SipRow* rowinfo, int64_t* counts,
+                            PlanStatus* status, hipStream_t s);
 
 hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr,
                        PlanStatus* status, hipStream_t s);
 
 hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
-                           const uint64_t* keepmask, const SipRow* rowinfo,
+                           const uint64_t* capmask, const uint64_t* keepmask,
+                           const SipRow* rowinfo,
                            const int64_t* rowptr, int32_t* idx, float* logw, double* p,
                            hipStream_t s);
 
-hipError_t launch_attention(const void* q, const void* k, const void* v, void* o,
-                            Dtype dt, int64_t B, int64_t H, int64_t N, int d,
+// fp32 -> bf16 (round to nearest even) of n elements, n a multiple of 8.
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+
+// Attention on bf16 q, k, v [B, H, N, d]; o is fp32 when out_f32, else bf16.
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                            bool out_f32, int64_t B, int64_t H, int64_t N, int d,
                             const int64_t* rowptr, const int32_t* idx,
                             const float* logw, bool dense, hipStream_t s);
 

@@ -30,11 +30,20 @@
 //     column, so the online-softmax rescale is lane-local.
 //   * Software pipeline with one barrier per tile: each wave issues tile
 //     t+1's S^T MFMAs next to tile t's softmax, then tile t's P V MFMAs. Two
-//     LDS buffers hold K and V of alternate tiles; K of tile t+2 is stored
-//     just before the barrier and V after it, and the gather of tile t+3
-//     into registers overlaps the whole next iteration. Two workgroups per CU. Block ids
-//     and log-weights come through scalar loads; gather addresses are 32-bit
-//     offsets from the head's base.
+//     LDS buffers hold K, V and log-weights of alternate tiles. The gather
+//     goes straight from global memory into LDS (global_load_lds_dwordx4,
+//     16 bytes per lane, no registers and no LDS store instructions): at the
+//     start of iteration t the waves issue K of tile t+2 and V of tile t+1
+//     into the buffers that iteration t-1 finished reading; each wave waits
+//     for its loads before the barrier that ends iteration t, which
+//     publishes them.
+//     Each lane picks the global address of the 16 bytes its LDS slot must
+//     hold, which is how the bank swizzles of both tiles are applied. Two
+//     workgroups per CU. Block ids come from one plan load per tile,
+//     broadcast with readlane; gather addresses are 32-bit offsets from the
+//     head's base.
+//   * fp32 inputs are rounded to bf16 by a separate pass before the kernel
+//     (round to nearest even, the rounding the products use either way).
 //   * Softmax per 4-key group: the group max of the raw products sets the
 //     tile max with one FMA per group, each weight is exp2 of one FMA
 //     (scale, log-weight and running max folded together), and the output
@@ -46,6 +55,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace absa {
 namespace {
@@ -98,20 +109,6 @@ __device__ __forceinline__ float half_sum(float x) {
 // exactly 1 in bf16, which raises the output error on concentrated attention
 // for a gain below 1%, so the max is always exact.
 
-// Per-lane prefetch registers for one tile: 16 bytes of K and of V at the
-// same (key, channel) position of the lane's KV block.
-template <int D, bool F32> struct TileRegs;
-template <int D> struct TileRegs<D, false> {
-    uint4 k[D / 32];
-    uint4 v[D / 32];
-    float lw[D / 32];
-};
-template <int D> struct TileRegs<D, true> {
-    float4 k[D / 32][2];
-    float4 v[D / 32][2];
-    float lw[D / 32];
-};
-
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -130,24 +127,49 @@ template <int D> __device__ __forceinline__ int vseg_swizzle(int key) {
     return (D == 128) ? (key & 3) : ((key >> 1) & 1);
 }
 
-template <int D, bool F32, bool DENSE>
+// K tiles are stored row-major [key][channel] without padding; 16-byte
+// column c of key row `key` sits at column c ^ kcol_swizzle(key), so that the
+// K operand reads (one column of 16 consecutive keys per 16 lanes) hit
+// distinct LDS banks.
+template <int D> __device__ __forceinline__ int kcol_swizzle(int key) {
+    return (D == 128) ? (key & 15) : ((key >> 1) & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+template <int V> using IntC = std::integral_constant<int, V>;
+
+// 16 bytes per lane from base + off straight into LDS: lane l's bytes land
+// at lds_dst + 16 l (global_load_lds_dwordx4, LDS base in M0). Written as
+// inline asm so that the compiler does not order every later LDS read of
+// the workgroup behind it; the loads complete under the kernel's own
+// s_waitcnt vmcnt(0) before the barrier that publishes them. The s_nop is
+// the wait state between the M0 write and its use by the load.
+__device__ __forceinline__ void load_to_lds(const char* base, uint32_t off, uint16_t* lds_dst) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D, bool OUT_F32, bool DENSE>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
-    constexpr int KS = D + 8;                   // K tile row stride (bf16)
-    constexpr int NP = D / 32;                  // loader passes per tile
-    constexpr int LPB = D / 2;                  // lanes per KV block in a pass
-    constexpr int BPP = 64 / LPB;               // blocks per pass per wave
     constexpr int NS = D / 16;                  // 16-channel MFMA steps
     constexpr int ND = D / 32;                  // 32-channel output blocks
-    constexpr int ESZ = F32 ? 4 : 2;            // bytes per input element
-    constexpr uint32_t BLOCK_BYTES = kKvBlock * D * ESZ;
-    __shared__ __align__(16) uint16_t Ks[2][kTileKeys * KS];
-    __shared__ __align__(16) uint16_t Vs[2][kTileKeys * D];
-    __shared__ float lws[2][kTileBlocks];
+    constexpr int ROWB = D * 2;                 // bytes of one bf16 key row
+    constexpr uint32_t BLOCK_BYTES = kKvBlock * ROWB;
+    constexpr int CPW = kTileKeys * ROWB / 1024 / 4;   // 1 KB gather chunks per wave
+    constexpr int KPC = 1024 / ROWB;            // key rows per chunk
+    __shared__ __align__(16) uint16_t Ks0[kTileKeys * D], Ks1[kTileKeys * D];
+    __shared__ __align__(16) uint16_t Vs0[kTileKeys * D], Vs1[kTileKeys * D];
+    __shared__ float lws0[kTileBlocks], lws1[kTileBlocks];
+    // Buffer b of each kind; b is a compile-time constant at every use.
+    auto Kbuf = [&](auto b) -> uint16_t* { if constexpr (decltype(b)::value) return Ks1; else return Ks0; };
+    auto Vbuf = [&](auto b) -> uint16_t* { if constexpr (decltype(b)::value) return Vs1; else return Vs0; };
+    auto Lbuf = [&](auto b) -> float* { if constexpr (decltype(b)::value) return lws1; else return lws0; };
 
     const int bid = blockIdx.x;
     const int64_t row = static_cast<int64_t>(bid % kXcds) * P.per_xcd + bid / kXcds;
     if (row >= P.rows) return;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,8 +180,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     const int64_t r = row - bh * P.QB;
     const int64_t q0 = r * kQueryBlock;
     const int64_t head_off = bh * P.N * D;
-    const char* kbase = static_cast<const char*>(P.k) + head_off * ESZ;
-    const char* vbase = static_cast<const char*>(P.v) + head_off * ESZ;
+    const char* kbase = static_cast<const char*>(P.k) + head_off * 2;
+    const char* vbase = static_cast<const char*>(P.v) + head_off * 2;
 
     int64_t base = 0, cnt = P.M;
     if (!DENSE) {
@@ -178,118 +200,62 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         for (int s = 0; s < NS; ++s) {
             const int dd = s * 16 + half * 8;
             uint4 u = make_uint4(0, 0, 0, 0);
-            if (ok) {
-                if constexpr (F32) {
-                    const float* src = static_cast<const float*>(P.q) + head_off + my_q * D + dd;
-                    const float4 x0 = *reinterpret_cast<const float4*>(src);
-                    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-                    u = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                   pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-                } else {
-                    u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
-                                                        head_off + my_q * D + dd);
-                }
-            }
+            if (ok)
+                u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) + head_off +
+                                                    my_q * D + dd);
             qb[s] = as_bf16x8(u);
         }
     }
 
-    // ---- gather of one tile into registers ----
-    // Wave w fetches tile blocks 4w..4w+3; lane (sub, c) of a pass covers
-    // block sub of the pass, K bytes [16c, 16c+16) of the block (key c/(D/8))
-    // and V channel pair c of its 4 keys. Block ids and log-weights are
-    // wave-uniform (scalar loads).
-    const int c = lane % LPB;
-    const int sub = lane / LPB;
-    const uint32_t k_lane_off = static_cast<uint32_t>(((c / (D / 8)) * D + (c % (D / 8)) * 8) * ESZ);
-    TileRegs<D, F32> R;
     // Plan entries of one tile: lane j < 16 holds block id j of the tile and
-    // lane 16 + j the bits of its fp32 log-weight: one coalesced load per
-    // tile (a single instruction with a per-lane address), fetched a tile
-    // ahead of the gather and broadcast to the wave with readlane.
-    int iv = 0;
-    auto load_plan = [&](int64_t t) {
-        if (DENSE) return;
+    // lane 16 + j the bits of its fp32 log-weight (one coalesced load per
+    // tile; entries past the row's end repeat its last entry).
+    auto load_plan = [&](int64_t t) -> int {
+        if (DENSE) return 0;
         const int64_t gb = t * kTileBlocks + (lane & 15);
         const int64_t e = base + ((gb < cnt) ? gb : (cnt - 1));
         const int* src = (lane & 16) ? reinterpret_cast<const int*>(P.logw) + e : P.idx + e;
-        iv = *src;
+        return *src;
     };
-    // Gather of one tile into registers; all K loads are issued before the V
-    // loads, so that storing K waits only for the K half.
-    auto load_tile = [&](int64_t t) {
-        const int t32 = static_cast<int>(t);
-        uint32_t boff[NP];
+    // Direct gather of K or V of tile T into buffer b. Wave w fills the 1 KB
+    // LDS chunks w*CPW .. w*CPW+CPW-1 of the tile; lane l's 16 bytes land at
+    // byte 16 l of its chunk, i.e. key row lkey, stored column lcol, and the
+    // lane loads the logical column that the swizzle puts there.
+    const int lkey = lane / (ROWB / 16);
+    const int lcol = lane % (ROWB / 16);
+    auto gather = [&](auto is_v, auto b, int ivt, int64_t T) {
+        constexpr bool ISV = decltype(is_v)::value;
+        const char* gsrc = ISV ? vbase : kbase;
+        uint16_t* dst = ISV ? Vbuf(b) : Kbuf(b);
+        const int T32 = static_cast<int>(T);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            int blk_s[BPP];
-            float lw_s[BPP];
-#pragma unroll
-            for (int j = 0; j < BPP; ++j) {
-                const int tb = wave * 4 + p * BPP + j;
-                const int gb = t32 * kTileBlocks + tb;
-                if (DENSE) {
-                    blk_s[j] = (gb < cnt32) ? gb : (cnt32 - 1);
-                    lw_s[j] = (gb < cnt32) ? 0.0f : -INFINITY;
-                } else {
-                    blk_s[j] = __builtin_amdgcn_readlane(iv, tb);
-                    const float lw = __int_as_float(__builtin_amdgcn_readlane(iv, 16 + tb));
-                    lw_s[j] = (gb < cnt32) ? lw * kLog2e : -INFINITY;
-                }
-            }
-            const int blk = (BPP == 1 || sub == 0) ? blk_s[0] : blk_s[BPP - 1];
-            R.lw[p] = (BPP == 1 || sub == 0) ? lw_s[0] : lw_s[BPP - 1];
-            boff[p] = static_cast<uint32_t>(blk) * BLOCK_BYTES + k_lane_off;
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const char* kp = kbase + static_cast<uint64_t>(boff[p]);
-            if constexpr (F32) {
-                R.k[p][0] = *reinterpret_cast<const float4*>(kp);
-                R.k[p][1] = *reinterpret_cast<const float4*>(kp + 16);
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = wave * CPW + i;
+            const int key = ch * KPC + lkey;                // key of the tile, 0..63
+            int blk;
+            if (DENSE) {
+                const int gb = T32 * kTileBlocks + (key >> 2);
+                blk = (gb < cnt32) ? gb : (cnt32 - 1);
+            } else if (KPC == 4) {
+                blk = __builtin_amdgcn_readlane(ivt, ch);   // the chunk is one block
             } else {
-                R.k[p] = *reinterpret_cast<const uint4*>(kp);
+                const int b0 = __builtin_amdgcn_readlane(ivt, 2 * ch);
+                const int b1 = __builtin_amdgcn_readlane(ivt, 2 * ch + 1);
+                blk = (lkey >= 4) ? b1 : b0;
             }
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const char* vp = vbase + static_cast<uint64_t>(boff[p]);
-            if constexpr (F32) {
-                R.v[p][0] = *reinterpret_cast<const float4*>(vp);
-                R.v[p][1] = *reinterpret_cast<const float4*>(vp + 16);
-            } else {
-                R.v[p] = *reinterpret_cast<const uint4*>(vp);
-            }
+            const int lc = ISV ? (lcol ^ (vseg_swizzle<D>(key) << 2)) : (lcol ^ kcol_swizzle<D>(key));
+            const uint32_t off = static_cast<uint32_t>(blk) * BLOCK_BYTES +
+                                 static_cast<uint32_t>((key & 3) * ROWB + lc * 16);
+            load_to_lds(gsrc, off, dst + ch * 512);
         }
     };
-    auto to_bf16x8 = [](const float4& a, const float4& b) {
-        return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                          pack_bf16x2(b.z, b.w));
-    };
-    auto store_k = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int tb = wave * 4 + p * BPP + sub;
-            const int key = tb * kKvBlock + c / (D / 8);
-            const int d0 = (c % (D / 8)) * 8;
-            uint4 ku;
-            if constexpr (F32) ku = to_bf16x8(R.k[p][0], R.k[p][1]);
-            else ku = R.k[p];
-            *reinterpret_cast<uint4*>(&Ks[buf][key * KS + d0]) = ku;
-        }
-    };
-    auto store_v = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int tb = wave * 4 + p * BPP + sub;
-            const int key = tb * kKvBlock + c / (D / 8);
-            const int d0 = (c % (D / 8)) * 8;
-            uint4 vu;
-            if constexpr (F32) vu = to_bf16x8(R.v[p][0], R.v[p][1]);
-            else vu = R.v[p];
-            const int vchunk = (d0 >> 3) ^ (vseg_swizzle<D>(key) << 2);
-            *reinterpret_cast<uint4*>(&Vs[buf][key * D + vchunk * 8]) = vu;
-            if (c == 0) lws[buf][tb] = R.lw[p];
+    // Log-weights of tile T (log2 units; -inf past the row's end) into buffer b.
+    auto write_lws = [&](auto b, int ivt, int64_t T) {
+        if (wave == 0 && (lane >> 4) == 1) {
+            const int j = lane - 16;
+            const bool ok = static_cast<int>(T) * kTileBlocks + j < cnt32;
+            const float lw = DENSE ? 0.0f : __int_as_float(ivt) * kLog2e;
+            Lbuf(b)[j] = ok ? lw : -INFINITY;
         }
     };
 
@@ -301,27 +267,34 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     const int trg = lane >> 4, rho = lane & 15;
     const int tr_row = 4 * (trg >> 1) + (rho >> 2);
     const int tr_swz = vseg_swizzle<D>(tr_row);
-    auto v_operand = [&](int buf, int j, int slice) {
+    auto v_operand = [&](auto b, int j, int slice) {
         const int chunk = ((j * 32 + 16 * (trg & 1) + 4 * (rho & 3)) >> 3) ^ (tr_swz << 2);
-        const uint16_t* p0 = &Vs[buf][(slice * 16 + tr_row) * D + chunk * 8 + (rho & 1) * 4];
+        const uint16_t* p0 = Vbuf(b) + (slice * 16 + tr_row) * D + chunk * 8 + (rho & 1) * 4;
         const uint2 lo = ds_read_tr16(p0);
         const uint2 hi = ds_read_tr16(p0 + 8 * D);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
 
+    // K operand of MFMA step s2 for key half kb: key row kb*32 + col,
+    // logical 16-byte column 2*s2 + half.
+    const int kswz0 = kcol_swizzle<D>(col), kswz1 = kcol_swizzle<D>(32 + col);
+    auto k_operand = [&](auto b, int kb, int s2) {
+        const int key = kb * 32 + col;
+        const int pc = (2 * s2 + half) ^ (kb ? kswz1 : kswz0);
+        return *reinterpret_cast<const uint4*>(Kbuf(b) + key * D + pc * 8);
+    };
+
     struct SAcc { floatx16 v[2]; };
     // S^T of one tile (64 keys x the wave's 32 queries).
-    auto qk = [&](int buf) {
+    auto qk = [&](auto b) {
         SAcc S;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             S.v[kb] = floatx16{};
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const uint4 a = *reinterpret_cast<const uint4*>(
-                    &Ks[buf][(kb * 32 + col) * KS + s * 16 + half * 8]);
-                S.v[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[s], S.v[kb], 0, 0, 0);
-            }
+            for (int s = 0; s < NS; ++s)
+                S.v[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k_operand(b, kb, s)),
+                                                                  qb[s], S.v[kb], 0, 0, 0);
         }
         return S;
     };
@@ -386,28 +359,46 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         }
     };
 
-    // Software pipeline over tiles (one barrier per tile). LDS buffer b holds
-    // K and V of tiles b, b+2, ...; iteration t runs tile t+1's S^T MFMAs
-    // alongside tile t's softmax, then tile t's P V MFMAs. K of tile t+2
-    // goes into the K half of buffer t%2 (free since tile t's S^T ran in
-    // iteration t-1) before the barrier, V of tile t+2 into the V half after
-    // it; the loads for tile t+3 are then issued.
-    if (ntiles > 0) { load_plan(0); load_tile(0); store_k(0); store_v(0); }
-    if (ntiles > 1) { load_plan(1); load_tile(1); store_k(1); store_v(1); }
+    // Software pipeline over tiles (one barrier per tile). Buffer b holds K,
+    // V and log-weights of tiles b, b+2, ...; iteration t runs tile t+1's
+    // S^T MFMAs alongside tile t's softmax, then tile t's P V MFMAs. It
+    // first issues the gathers of K of tile t+2 (into buffer t%2, whose K
+    // was read by the S^T MFMAs of iteration t-1) and of V and log-weights of
+    // tile t+1 (into buffer (t+1)%2, read in iteration t-1), and the plan
+    // entries of tile t+3.
+    int iv1 = 0, iv2 = 0;
+    {
+        const int iv0 = (ntiles > 0) ? load_plan(0) : 0;
+        iv1 = (ntiles > 1) ? load_plan(1) : 0;
+        iv2 = (ntiles > 2) ? load_plan(2) : 0;
+        if (ntiles > 0) {
+            gather(IntC<0>{}, IntC<0>{}, iv0, 0);
+            gather(IntC<1>{}, IntC<0>{}, iv0, 0);
+            write_lws(IntC<0>{}, iv0, 0);
+        }
+        if (ntiles > 1) gather(IntC<0>{}, IntC<1>{}, iv1, 1);
+    }
+    wait_lds_loads();
     __syncthreads();
-    if (ntiles > 2) { load_plan(2); load_tile(2); }
-    if (ntiles > 3) load_plan(3);
     // Every wave runs the same instruction stream (a wave whose queries lie
     // past N computes on zero queries and stores nothing), which keeps the
     // loop free of branches around its loads and MFMAs.
-    SAcc Sa = qk(0);
+    SAcc Sa = qk(IntC<0>{});
     // every wave has read K of tile 0 before iteration 0 overwrites it
     __syncthreads();
-    // One pipeline step on tile t: Scur holds S^T of tile t, Snext receives
-    // S^T of tile t+1. The loop runs two steps per iteration with the roles
-    // of the two accumulator sets swapped, so no registers are copied.
-    auto step = [&](int64_t t, SAcc& Scur, SAcc& Snext) {
-        const int buf = static_cast<int>(t & 1);
+    // One pipeline step on tile t (buffer b = t % 2): Scur holds S^T of tile
+    // t, Snext receives S^T of tile t+1. The loop runs two steps per
+    // iteration with the roles of the two accumulator sets swapped, so no
+    // registers are copied.
+    auto step = [&](auto b, int64_t t, SAcc& Scur, SAcc& Snext) {
+        constexpr int buf = decltype(b)::value;
+        const IntC<buf ^ 1> nb{};
+        if (t + 2 < ntiles) gather(IntC<0>{}, b, iv2, t + 2);
+        if (t + 1 < ntiles) {
+            gather(IntC<1>{}, nb, iv1, t + 1);
+            write_lws(nb, iv1, t + 1);
+        }
+        const int ivn = (t + 3 < ntiles) ? load_plan(t + 3) : 0;
         {
             // Phase A: S^T of tile t+1 (from the other buffer; on the last
             // tile that is stale K and the result is never used), one MFMA
@@ -422,16 +413,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) st.lwv[kb][g] = lws[buf][kb * 8 + 2 * g + half];
+                for (int g = 0; g < 4; ++g) st.lwv[kb][g] = Lbuf(b)[kb * 8 + 2 * g + half];
             }
             constexpr int QS = 2 * NS;
             // step i: key half i&1 (the two accumulator chains alternate),
             // channel step i>>1
-            auto kread = [&](int i) {
-                const int kb = i & 1, s2 = i >> 1;
-                return *reinterpret_cast<const uint4*>(
-                    &Ks[buf ^ 1][(kb * 32 + col) * KS + s2 * 16 + half * 8]);
-            };
+            auto kread = [&](int i) { return k_operand(nb, i & 1, i >> 1); };
             uint4 ka[QS];
             ka[0] = kread(0);
             ka[1] = kread(1);
@@ -478,11 +465,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
             constexpr int PHALF = 2 * ND;
             auto pv_at = [](int c) { return c < PHALF ? (c / ND) : 2 + (c - PHALF) / ND; };
             uint4 va[PS];
-            va[0] = v_operand(buf, 0 % ND, pv_at(0));
-            va[1] = v_operand(buf, 1 % ND, pv_at(1));
+            va[0] = v_operand(b, 0 % ND, pv_at(0));
+            va[1] = v_operand(b, 1 % ND, pv_at(1));
 #pragma unroll
             for (int c = 0; c < PS; ++c) {
-                if (c + 2 < PS) va[c + 2] = v_operand(buf, (c + 2) % ND, pv_at(c + 2));
+                if (c + 2 < PS) va[c + 2] = v_operand(b, (c + 2) % ND, pv_at(c + 2));
                 const int j = c % ND, sl = pv_at(c);
                 O[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(va[c]), as_bf16x8(make_uint4(pw[sl][0], pw[sl][1], pw[sl][2], pw[sl][3])),
@@ -495,21 +482,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             l_run = fmaf(l_run, st.alpha, (st.psum[0] + st.psum[1]) + (st.psum[2] + st.psum[3]));
-            // K of tile t+2, as late as the barrier allows (unconditional:
-            // past the row's end it writes stale K that only the discarded
-            // S^T of the last tile reads)
-            store_k(buf);
         }
+        // This wave's gathers are complete; after the barrier every wave's
+        // gathers of this iteration are visible.
+        wait_lds_loads();
         __syncthreads();
-        // V of tile t+2 (past the row's end: stale data nobody reads)
-        store_v(buf);
-        if (t + 3 < ntiles) load_tile(t + 3);
-        if (t + 4 < ntiles) load_plan(t + 4);
+        iv1 = iv2;
+        iv2 = ivn;
     };
     SAcc Sb;
     for (int64_t t = 0; t < ntiles; t += 2) {
-        step(t, Sa, Sb);
-        if (t + 1 < ntiles) step(t + 1, Sb, Sa);
+        step(IntC<0>{}, t, Sa, Sb);
+        if (t + 1 < ntiles) step(IntC<1>{}, t + 1, Sb, Sa);
     }
 
     const float l_tot = half_sum(l_run);
@@ -522,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
             const int dd = j * 32 + g * 8 + half * 4;
             const float x0 = O[j][g * 4 + 0] * inv, x1 = O[j][g * 4 + 1] * inv;
             const float x2 = O[j][g * 4 + 2] * inv, x3 = O[j][g * 4 + 3] * inv;
-            if constexpr (F32) {
+            if constexpr (OUT_F32) {
                 float* dst = static_cast<float*>(P.o) + head_off + my_q * D + dd;
                 *reinterpret_cast<float4*>(dst) = make_float4(x0, x1, x2, x3);
             } else {
@@ -533,18 +517,40 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     }
 }
 
-template <int D, bool F32, bool DENSE>
+template <int D, bool OUT_F32, bool DENSE>
 void launch_one(const AttnParams& p, hipStream_t s) {
     const int64_t grid = p.per_xcd * kXcds;
-    hipLaunchKernelGGL((attn_kernel<D, F32, DENSE>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, OUT_F32, DENSE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(256), 0, s, p);
+}
+
+// fp32 -> bf16, round to nearest even; 8 elements per thread and iteration.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src,
+                                                      uint16_t* __restrict__ dst, int64_t n8) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n8; i += static_cast<int64_t>(gridDim.x) * 256) {
+        const float4 a = reinterpret_cast<const float4*>(src)[2 * i];
+        const float4 b = reinterpret_cast<const float4*>(src)[2 * i + 1];
+        reinterpret_cast<uint4*>(dst)[i] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                                      pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+    }
 }
 
 }  // namespace
 
-hipError_t launch_attention(const void* q, const void* k, const void* v, void* o, Dtype dt,
-                            int64_t B, int64_t H, int64_t N, int d, const int64_t* rowptr,
-                            const int32_t* idx, const float* logw, bool dense, hipStream_t s) {
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+    const int64_t n8 = n / 8;                   // n is a multiple of 8 (d in {64, 128})
+    if (n8 == 0) return hipSuccess;
+    int64_t blocks = (n8 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src,
+                       dst, n8);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                            bool out_f32, int64_t B, int64_t H, int64_t N, int d,
+                            const int64_t* rowptr, const int32_t* idx, const float* logw,
+                            bool dense, hipStream_t s) {
     AttnParams p;
     p.q = q; p.k = k; p.v = v; p.o = o;
     p.N = N;
@@ -555,12 +561,11 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, void* o
     p.rowptr = rowptr; p.idx = idx; p.logw = logw;
     p.scale_log2 = kLog2e / sqrtf(static_cast<float>(d));
     if (p.rows == 0) return hipSuccess;
-    const bool f32 = (dt == kF32);
     if (d == 128) {
-        if (f32) dense ? launch_one<128, true, true>(p, s) : launch_one<128, true, false>(p, s);
+        if (out_f32) dense ? launch_one<128, true, true>(p, s) : launch_one<128, true, false>(p, s);
         else dense ? launch_one<128, false, true>(p, s) : launch_one<128, false, false>(p, s);
     } else {
-        if (f32) dense ? launch_one<64, true, true>(p, s) : launch_one<64, true, false>(p, s);
+        if (out_f32) dense ? launch_one<64, true, true>(p, s) : launch_one<64, true, false>(p, s);
         else dense ? launch_one<64, false, true>(p, s) : launch_one<64, false, false>(p, s);
     }
     return hipGetLastError();

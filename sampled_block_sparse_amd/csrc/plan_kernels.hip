@@ -596,7 +596,9 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // that capped something, and a round's new caps are the blocks with
 // thr <= s_j < thr_min: one fp32 comparison per block and round, and no
 // per-block cap state. The row's outcome (mode, c, thr_min) goes to rowinfo,
-// its keep mask (one bit per block, from the Philox draws) to keepmask.
+// its keep mask (one bit per block, from the Philox draws) to keepmask and
+// its cap mask (s_j >= thr_min) to capmask, so the fill kernel reads the
+// score only of kept blocks that are not capped.
 // ---------------------------------------------------------------------------
 constexpr int kSipThreads = 512;
 constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
@@ -604,8 +606,8 @@ constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
 template <bool LDS_ROW>
 __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
-    uint64_t seed, uint64_t* __restrict__ keepmask, SipRow* __restrict__ rowinfo,
-    int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
+    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     extern __shared__ float sv[];
     __shared__ double redd[kSipThreads / 64];
     __shared__ int redi[kSipThreads / 64];
@@ -613,6 +615,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
     uint64_t* km = keepmask + row * words;
+    uint64_t* cm = capmask + row * words;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     auto score = [&](int64_t j) { return LDS_ROW ? sv[j] : sg[j]; };
@@ -678,13 +681,18 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     int kept = 0;
     for (int64_t base = 0; base < M; base += kSipThreads) {
         const int64_t j = base + tid;
-        bool keep = false;
+        bool keep = false, capped = false;
         if (j < M) {
             const float v = score(j);
-            keep = sip_uniform(seed, b, h, r, j) < sip_p(v >= thr_min, ri, v);
+            capped = v >= thr_min;
+            keep = sip_uniform(seed, b, h, r, j) < sip_p(capped, ri, v);
         }
         const uint64_t kb = __ballot(keep);
-        if (lane == 0 && base + wave * 64 < M) km[(base >> 6) + wave] = kb;
+        const uint64_t cb = __ballot(capped);
+        if (lane == 0 && base + wave * 64 < M) {
+            km[(base >> 6) + wave] = kb;
+            cm[(base >> 6) + wave] = cb;
+        }
         kept += keep ? 1 : 0;
     }
     const int tk = block_sum(kept, redi);
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
 // a 256-word chunk; an exclusive scan of the words' popcounts gives each
 // thread the position of its first kept block.
 __global__ __launch_bounds__(256) void sip_fill_kernel(
-    const float* __restrict__ scores, int64_t M,
+    const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
     const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
     const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
     double* __restrict__ p_out) {
@@ -741,6 +749,7 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
+    const uint64_t* cm = capmask + row * words;
     const uint64_t* km = keepmask + row * words;
     const SipRow ri = rowinfo[row];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -748,6 +757,7 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     for (int64_t base = 0; base < words; base += 256) {
         const int64_t w = base + tid;
         const uint64_t kw = (w < words) ? km[w] : 0ull;
+        const uint64_t cw = (w < words) ? cm[w] : 0ull;
         const int pc = __popcll(kw);
         int incl = pc;
 #pragma unroll
@@ -768,8 +778,8 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
             const int bit = __ffsll(static_cast<long long>(bits)) - 1;
             bits &= bits - 1;
             const int64_t j = w * 64 + bit;
-            const float v = sg[j];
-            const double p = sip_p(v >= ri.thr, ri, v);
+            const bool capped = (cw >> bit) & 1ull;
+            const double p = capped ? 1.0 : sip_p(false, ri, sg[j]);
             idx[at] = static_cast<int32_t>(j);
             logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
             p_out[at] = p;
@@ -895,8 +905,8 @@ hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar
 }
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
-                            int64_t budget, uint64_t seed, uint64_t* keepmask, SipRow* rowinfo,
-                            int64_t* counts, PlanStatus* status, hipStream_t s) {
+                            int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
+                            SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
     if (M <= kSipLdsMaxBlocks) {
         const size_t shm = static_cast<size_t>(M) * sizeof(float);
@@ -906,12 +916,13 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
         if (e != hipSuccess) return e;
         return launch_checked([&] {
             hipLaunchKernelGGL(sip_count_kernel<true>, dim3(rows), dim3(kSipThreads), shm, s,
-                               scores, H, QB, M, budget, seed, keepmask, rowinfo, counts, status);
+                               scores, H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts,
+                               status);
         });
     }
     return launch_checked([&] {
         hipLaunchKernelGGL(sip_count_kernel<false>, dim3(rows), dim3(kSipThreads), 0, s, scores,
-                           H, QB, M, budget, seed, keepmask, rowinfo, counts, status);
+                           H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts, status);
     });
 }
 
@@ -922,12 +933,12 @@ hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr, Pla
     });
 }
 
-hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
+hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M, const uint64_t* capmask,
                            const uint64_t* keepmask, const SipRow* rowinfo, const int64_t* rowptr,
                            int32_t* idx, float* logw, double* p, hipStream_t s) {
     return launch_checked([&] {
-        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, keepmask,
-                           rowinfo, rowptr, idx, logw, p);
+        hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, capmask,
+                           keepmask, rowinfo, rowptr, idx, logw, p);
     });
 }
 

@@ -237,6 +237,46 @@ def test_pool_reuse_and_release():
     absa.absa_release_cached_memory()
 
 
+def _sip_edge_rows(M=256, K=16):
+    """Rows whose water-filling decisions sit on rounding edges: blocks with
+    c*q exactly 1 in real arithmetic (and one fp32 ulp either side), ties,
+    zeros and scores below 2^-52 (q = 0), a cascade of many capping rounds,
+    an all-capped-then-zero row (mode 1), and random rows."""
+    rng = np.random.default_rng(2024)
+    rows = []
+    n = K // 2
+    y = np.float32(2.0 ** -12)
+    x = np.float32((M - n) / (K - n)) * y                 # c * x == 1 exactly in reals
+    for xb in (x, np.nextafter(x, np.float32(1)), np.nextafter(x, np.float32(0))):
+        r = np.full(M, y, np.float32)
+        r[rng.choice(M, n, replace=False)] = xb
+        rows.append(r)
+    rows.append(np.full(M, np.float32(1.0 / M), np.float32))          # ties, no cap
+    r = np.zeros(M, np.float32)
+    r[5] = 1.0
+    r[6:40] = np.float32(1e-20)                                       # q = 0
+    r[40:60] = np.float32(2.0 ** -52)
+    rows.append(r)
+    r = np.zeros(M, np.float32)
+    r[:K - 1] = np.float32(0.01)                                      # capped, then S = 0
+    rows.append(r)
+    rows.append((2.0 ** -np.arange(1, M + 1, dtype=np.float64) * 0.999).astype(np.float32))
+    r = rng.random(M).astype(np.float32)
+    rows.append((r / r.sum() * np.float32(0.999)).astype(np.float32))
+    return np.stack(rows)[None, None]                                 # [1, 1, QB=8, M]
+
+
+@pytest.mark.parametrize("K", [1, 16, 100, 255, 256])
+def test_sip_rounding_edges_bit_exact(K):
+    s32 = _sip_edge_rows()
+    assert s32.shape == (1, 1, 8, 256)
+    N, d = 1024, 64
+    seed = 0x5EED0042
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, K, seed)
+    ref = oracle.plan_from_scores(s32, 1, 1, N, d, K, seed)
+    check_plan_exact(plan.export(), ref, f"edge rows K={K}")
+
+
 def test_plan_mismatch_and_bad_scores():
     q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=64, seed=9))
     plan = absa.absa_plan_create(q, k, 10, 1)
