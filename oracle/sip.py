@@ -24,9 +24,11 @@ Readings where the pages are silent:
         if Z is empty: p_j = c * q_j on U, stop;
         p = 1 on Z, t += |Z|, U -= Z.
   * sampling design = Poisson: one independent Bernoulli(p_j) per block, so
-    the count per row varies around K; the draw uses one uniform
-    u = Philox4x32-10(key = (seed_lo, seed_hi), counter = (j, r, h, b)),
-    u = ((x0 << 32 | x1) >> 11) * 2^-53, and keeps block j iff u < p_j;
+    the count per row varies around K; the draw uses one uniform per block
+    from Philox4x32-10(key = (seed_lo, seed_hi), counter = (j >> 1, r, h, b)):
+    one call yields four 32-bit words (x0, x1, x2, x3), block 2i takes
+    (hi, lo) = (x0, x1) and block 2i+1 takes (x2, x3), u = ((hi << 32 | lo)
+    >> 11) * 2^-53, and block j is kept iff u < p_j;
   * the Horvitz-Thompson weight 1/p enters as the logit offset
     logw = -ln(p) (natural log, fp64, rounded to fp32; +0 for p = 1).
 """
@@ -82,10 +84,15 @@ def sip_probabilities(s32: np.ndarray, budget: int) -> np.ndarray:
 
 
 def sip_uniforms(seed: int, b: int, h: int, r: int, M: int) -> np.ndarray:
-    """u_j in [0, 1) for j < M from Philox4x32-10, key = seed, counter = (j, r, h, b)."""
+    """u_j in [0, 1) for j < M: Philox4x32-10 with key = seed and counter
+    (j >> 1, r, h, b); even j takes output words 0 and 1, odd j words 2 and 3."""
     j = np.arange(M, dtype=np.uint64)
-    x0, x1, _, _ = philox4x32_10(j, r, h, b, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    u53 = ((x0 << np.uint64(32)) | x1) >> np.uint64(11)
+    x0, x1, x2, x3 = philox4x32_10(j >> np.uint64(1), r, h, b, seed & 0xFFFFFFFF,
+                                   (seed >> 32) & 0xFFFFFFFF)
+    odd = (j & np.uint64(1)).astype(bool)
+    hi = np.where(odd, x2, x0)
+    lo = np.where(odd, x3, x1)
+    u53 = ((hi << np.uint64(32)) | lo) >> np.uint64(11)
     return u53.astype(np.float64) * (2.0 ** -53)
 
 

@@ -512,6 +512,25 @@ template <typename V> __device__ V block_sum(V v, V* red) {
     return t;
 }
 
+// An int and a double summed over the block with one pair of barriers.
+__device__ void block_sum2(int a, double b, int* redi, double* redd, int& ta, double& tb) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        redi[wave] = a;
+        redd[wave] = b;
+    }
+    __syncthreads();
+    ta = 0;
+    tb = 0.0;
+    for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) {
+        ta += redi[k];
+        tb += redd[k];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): 4-word counter, 2-word
 // key; 10 rounds of two 32x32->64 multiplies with the Weyl key schedule.
@@ -532,15 +551,29 @@ __device__ __forceinline__ void philox_10(uint32_t c[4], uint32_t k0, uint32_t k
     }
 }
 
-// Uniform in [0, 1) for KV block j of row (b, h, r): 53 high bits of the
-// first two output words.
-__device__ __forceinline__ double sip_uniform(uint64_t seed, int64_t b, int64_t h, int64_t r,
-                                              int64_t j) {
-    uint32_t c[4] = {static_cast<uint32_t>(j), static_cast<uint32_t>(r),
+// Uniforms in [0, 1) for KV blocks 2i and 2i+1 of row (b, h, r): one
+// Philox call with counter (i, r, h, b); block 2i takes the 53 high bits of
+// output words 0 and 1, block 2i+1 those of words 2 and 3.
+__device__ __forceinline__ void sip_uniform_pair(uint64_t seed, int64_t b, int64_t h, int64_t r,
+                                                 int64_t i, double& u0, double& u1) {
+    uint32_t c[4] = {static_cast<uint32_t>(i), static_cast<uint32_t>(r),
                      static_cast<uint32_t>(h), static_cast<uint32_t>(b)};
     philox_10(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
-    const uint64_t u53 = ((static_cast<uint64_t>(c[0]) << 32) | c[1]) >> 11;
-    return static_cast<double>(u53) * 0x1.0p-53;
+    u0 = static_cast<double>(((static_cast<uint64_t>(c[0]) << 32) | c[1]) >> 11) * 0x1.0p-53;
+    u1 = static_cast<double>(((static_cast<uint64_t>(c[2]) << 32) | c[3]) >> 11) * 0x1.0p-53;
+}
+
+// Bit k of a goes to bit 2k, bit k of b to bit 2k+1 (32 bits each).
+__device__ __forceinline__ uint64_t interleave_bits(uint32_t a, uint32_t b) {
+    auto spread = [](uint64_t x) {
+        x = (x | (x << 16)) & 0x0000FFFF0000FFFFull;
+        x = (x | (x << 8)) & 0x00FF00FF00FF00FFull;
+        x = (x | (x << 4)) & 0x0F0F0F0F0F0F0F0Full;
+        x = (x | (x << 2)) & 0x3333333333333333ull;
+        x = (x | (x << 1)) & 0x5555555555555555ull;
+        return x;
+    };
+    return spread(a) | (spread(b) << 1);
 }
 
 // floor(s * 2^52) of an fp32 score in [0, 1], as an exact fp64 integer. Sums
@@ -586,8 +619,10 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // SIP probabilities and draws [hamidun, SIP paragraph; edumints, SIP item]:
 // capped water-filling in exact fixed point (q_j = floor(s_j 2^52), exact
 // sums, IEEE double division and product), then one Poisson draw per block.
-// One workgroup per plan row; with LDS_ROW the row's scores are staged in
-// LDS, otherwise every pass re-reads them from global memory.
+// One workgroup of 512 threads per plan row. Thread t owns the block pairs
+// (2i, 2i+1) with i = t + 512 k; with MAXP > 0 it keeps their scores in
+// registers (rows of up to 1024 * MAXP blocks), otherwise every pass
+// re-reads them from global memory.
 //
 // A round of the water-filling caps the still-active blocks with
 // fl(c q_j) >= 1, i.e. q_j >= T(c) (cap_threshold), i.e. s_j >= thr(c) for
@@ -601,14 +636,14 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // score only of kept blocks that are not capped.
 // ---------------------------------------------------------------------------
 constexpr int kSipThreads = 512;
-constexpr int kSipLdsMaxBlocks = 36864;          // 144 KB of scores
+constexpr int kSipPairsPerPass = kSipThreads;            // block pairs per pass
+constexpr int kSipMaxPairs = 32;                         // register-resident rows: M <= 32768
 
-template <bool LDS_ROW>
+template <int MAXP>
 __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
     uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
-    extern __shared__ float sv[];
     __shared__ double redd[kSipThreads / 64];
     __shared__ int redi[kSipThreads / 64];
     const int64_t row = blockIdx.x;
@@ -618,15 +653,49 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     uint64_t* cm = capmask + row * words;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    auto score = [&](int64_t j) { return LDS_ROW ? sv[j] : sg[j]; };
+    const int M32 = static_cast<int>(M);                  // M < 2^19
+    const int npairs = (M32 + 1) / 2;
+    const int npass = (npairs + kSipPairsPerPass - 1) / kSipPairsPerPass;
+    // Scores of pair i (blocks past M read as -1: never capped, never kept).
+    auto load_pair = [&](int i) {
+        const int j = 2 * i;
+        return make_float2(j < M32 ? sg[j] : -1.0f, j + 1 < M32 ? sg[j + 1] : -1.0f);
+    };
+    // register copies of the thread's pairs (two plain arrays so that they
+    // stay in registers)
+    float sx[MAXP > 0 ? MAXP : 1], sy[MAXP > 0 ? MAXP : 1];
+    auto pair_at = [&](int k) {
+        if constexpr (MAXP > 0) return make_float2(sx[k], sy[k]);
+        else return load_pair(tid + k * kSipPairsPerPass);
+    };
 
     double sum = 0.0;
     int bad = 0;
-    for (int64_t j = tid; j < M; j += kSipThreads) {
-        const float v = sg[j];
+    float vmax = -1.0f;            // largest score of this thread not yet capped
+    auto add_score = [&](float v, int j) {
+        if (j >= M32) return;
         if (!(v >= 0.0f && v <= 1.0f)) bad = 1;
         else sum += fixed_point(v);
-        if (LDS_ROW) sv[j] = v;
+        vmax = fmaxf(vmax, v);
+    };
+    if constexpr (MAXP > 0) {
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int i = tid + k * kSipPairsPerPass;
+            const float2 v = (k < npass) ? load_pair(i) : make_float2(-1.0f, -1.0f);
+            sx[k] = v.x;
+            sy[k] = v.y;
+            add_score(v.x, 2 * i);
+            add_score(v.y, 2 * i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        for (int k = 0; k < npass; ++k) {
+            const int i = tid + k * kSipPairsPerPass;
+            const float2 v = load_pair(i);
+            add_score(v.x, 2 * i);
+            add_score(v.y, 2 * i + 1);
+        }
     }
     const double total = block_sum(sum, redd);
     const int nbad = block_sum(bad, redi);
@@ -657,20 +726,56 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         const float thr = fp32_at_least(cap_threshold(c) * 0x1.0p-52);
         int ncap = 0;
         double scap = 0.0;
-        for (int64_t j = tid; j < M; j += kSipThreads) {
-            const float v = score(j);
+        auto test = [&](float v) {
+            // opaque copy: keeps fixed_point(v) of every block from being
+            // hoisted out of the rounds loop (64 live doubles otherwise)
+            asm volatile("" : "+v"(v));
             if (v >= thr && v < thr_min) {
                 ++ncap;
                 scap += fixed_point(v);
             }
+        };
+        if constexpr (MAXP > 0) {
+            // a wave none of whose uncapped scores reaches thr has no new cap
+            if (__builtin_amdgcn_ballot_w64(vmax >= thr) != 0) {
+#pragma unroll
+                for (int k = 0; k < MAXP; ++k) {
+                    test(sx[k]);
+                    test(sy[k]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            for (int k = 0; k < npass; ++k) {
+                const float2 v = pair_at(k);
+                test(v.x);
+                test(v.y);
+            }
         }
-        const int tcap = block_sum(ncap, redi);
-        const double tsum = block_sum(scap, redd);
+        // both round totals in one block reduction (the fixed-point sums are
+        // integers below 2^53, exact in any order)
+        int tcap;
+        double tsum;
+        block_sum2(ncap, scap, redi, redd, tcap, tsum);
         if (tcap == 0) { ri.mode = 2; ri.c = c; break; }
         taken += tcap;
         n_active -= tcap;
         S -= tsum;
         thr_min = fminf(thr_min, thr);
+        if constexpr (MAXP > 0) {
+            // this thread's largest score below the new thr_min
+            if (__builtin_amdgcn_ballot_w64(vmax >= thr_min) != 0) {
+                float m = -1.0f;
+#pragma unroll
+                for (int k = 0; k < MAXP; ++k) {
+                    float x = sx[k], y = sy[k];
+                    asm volatile("" : "+v"(x), "+v"(y));
+                    m = x < thr_min ? fmaxf(m, x) : m;
+                    m = y < thr_min ? fmaxf(m, y) : m;
+                }
+                vmax = m;
+            }
+        }
     }
     ri.thr = thr_min;
 
@@ -679,21 +784,40 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const int64_t h = bidx % H;
     const int64_t b = bidx / H;
     int kept = 0;
-    for (int64_t base = 0; base < M; base += kSipThreads) {
-        const int64_t j = base + tid;
-        bool keep = false, capped = false;
-        if (j < M) {
-            const float v = score(j);
-            capped = v >= thr_min;
-            keep = sip_uniform(seed, b, h, r, j) < sip_p(capped, ri, v);
+    // Pass k covers blocks [1024 k, 1024 k + 1024); wave w's lanes hold the
+    // pairs of blocks [1024 k + 128 w, +128), i.e. mask words 16 k + 2 w and
+    // 16 k + 2 w + 1, whose bits interleave the even- and odd-block ballots.
+    auto draw = [&](int k, float2 v) {
+        const int i = tid + k * kSipPairsPerPass;
+        double u0 = 1.0, u1 = 1.0;
+        sip_uniform_pair(seed, b, h, r, i, u0, u1);
+        const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
+        const bool keep0 = 2 * i < M32 && u0 < sip_p(cap0, ri, v.x);
+        const bool keep1 = 2 * i + 1 < M32 && u1 < sip_p(cap1, ri, v.y);
+        const uint64_t ke = __ballot(keep0), ko = __ballot(keep1);
+        const uint64_t ce = __ballot(cap0), co = __ballot(cap1);
+        if (lane == 0) {
+            const int w0 = 16 * k + 2 * wave;
+            if (w0 < words) {
+                km[w0] = interleave_bits(static_cast<uint32_t>(ke), static_cast<uint32_t>(ko));
+                cm[w0] = interleave_bits(static_cast<uint32_t>(ce), static_cast<uint32_t>(co));
+            }
+            if (w0 + 1 < words) {
+                km[w0 + 1] = interleave_bits(static_cast<uint32_t>(ke >> 32), static_cast<uint32_t>(ko >> 32));
+                cm[w0 + 1] = interleave_bits(static_cast<uint32_t>(ce >> 32), static_cast<uint32_t>(co >> 32));
+            }
         }
-        const uint64_t kb = __ballot(keep);
-        const uint64_t cb = __ballot(capped);
-        if (lane == 0 && base + wave * 64 < M) {
-            km[(base >> 6) + wave] = kb;
-            cm[(base >> 6) + wave] = cb;
+        kept += (keep0 ? 1 : 0) + (keep1 ? 1 : 0);
+    };
+    if constexpr (MAXP > 0) {
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            if (k < npass) draw(k, make_float2(sx[k], sy[k]));
+            // one pair's Philox at a time: keeps the register count low
+            __builtin_amdgcn_sched_barrier(0);
         }
-        kept += keep ? 1 : 0;
+    } else {
+        for (int k = 0; k < npass; ++k) draw(k, pair_at(k));
     }
     const int tk = block_sum(kept, redi);
     if (tid == 0) {
@@ -908,21 +1032,18 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
                             int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
                             SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
-    if (M <= kSipLdsMaxBlocks) {
-        const size_t shm = static_cast<size_t>(M) * sizeof(float);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sip_count_kernel<true>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(kSipLdsMaxBlocks * sizeof(float)));
-        if (e != hipSuccess) return e;
-        return launch_checked([&] {
-            hipLaunchKernelGGL(sip_count_kernel<true>, dim3(rows), dim3(kSipThreads), shm, s,
-                               scores, H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts,
-                               status);
-        });
-    }
+    const int64_t npass = ((M + 1) / 2 + kSipPairsPerPass - 1) / kSipPairsPerPass;
     return launch_checked([&] {
-        hipLaunchKernelGGL(sip_count_kernel<false>, dim3(rows), dim3(kSipThreads), 0, s, scores,
-                           H, QB, M, budget, seed, capmask, keepmask, rowinfo, counts, status);
+#define ABSA_SIP_LAUNCH(MP)                                                                      \
+    hipLaunchKernelGGL(sip_count_kernel<MP>, dim3(rows), dim3(kSipThreads), 0, s, scores, H, QB, \
+                       M, budget, seed, capmask, keepmask, rowinfo, counts, status)
+        if (npass <= 8) ABSA_SIP_LAUNCH(8);
+        else if (npass <= 16) ABSA_SIP_LAUNCH(16);
+        else if (npass <= 20) ABSA_SIP_LAUNCH(20);
+        else if (npass <= 24) ABSA_SIP_LAUNCH(24);
+        else if (npass <= kSipMaxPairs) ABSA_SIP_LAUNCH(kSipMaxPairs);
+        else ABSA_SIP_LAUNCH(0);
+#undef ABSA_SIP_LAUNCH
     });
 }
 
