@@ -90,13 +90,16 @@ __global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kb
 // assignment (C_eff = min(C, n); further clusters are zero with weight 0).
 //
 // Layout: the queries stay in LDS in their storage type (bf16 or fp32, both
-// exact in fp64); thread (i, h) keeps query i in registers and computes its
-// distances to the CH clusters h*CH .. h*CH+CH-1 with CH independent fp64
-// FMA chains, reading the centroids from a [d][16] fp64 LDS array by
-// broadcast. The update ranks each cluster's members with wave ballots and
-// sums only members, so it costs n*d adds. The centroid sums of bf16/fp32
-// inputs are exact in fp64 for any realistic exponent spread, so each
-// centroid is the correctly rounded mean whatever the summation order.
+// exact in fp64). The nearest centroid minimises |c_m|^2 - 2 q.c_m (the
+// query's own |q|^2 is common to all clusters): thread (i, hd) forms the
+// fp64 dot products of query i with every cluster over channel half hd,
+// reading the centroids from a [d][NC] fp64 LDS array by broadcast; the two
+// halves are added in a fixed order. The rounding differs from summing
+// (q - c)^2 only far below the near-tie margins that decide an assignment.
+// The update ranks each cluster's members with wave ballots and sums only
+// members, so it costs n*d adds. The centroid sums of bf16/fp32 inputs are
+// exact in fp64 for any realistic exponent spread, so each centroid is the
+// correctly rounded mean whatever the summation order.
 // ---------------------------------------------------------------------------
 template <typename T> struct QStore;
 template <> struct QStore<uint16_t> {
@@ -115,14 +118,16 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
                                                      int64_t QB, int C, int iters,
                                                      float* __restrict__ cent_out,
                                                      float* __restrict__ w_out) {
+    constexpr int NC = 2 * CH;                          // cluster slots
     constexpr int QS = D + QStore<T>::kPad;
+    constexpr int DH = D / 2;                           // channels per half
     __shared__ T qs[kQueryBlock * QS];
-    __shared__ __align__(16) double ct[D][2 * CH];      // centroids, transposed
-    __shared__ double bdist[2][kQueryBlock];
-    __shared__ int bidx[2][kQueryBlock];
-    __shared__ int assign[kQueryBlock];
-    __shared__ int wcnt[2][2 * CH];
-    __shared__ int counts[2 * CH], offs[2 * CH];
+    __shared__ __align__(16) double ct[D][NC];          // centroids, transposed
+    __shared__ double part[NC][kQueryBlock];            // dot products over channel half 1
+    __shared__ double cc[NC];                           // |c_m|^2
+    __shared__ int assign[kQueryBlock], rank_in_wave[kQueryBlock];
+    __shared__ int wcnt[2][NC];
+    __shared__ int counts[NC], offs[NC];
     __shared__ int members[kQueryBlock];
 
     const int64_t row = blockIdx.x;
@@ -140,49 +145,53 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
         qs[i * QS + dd] = qrow[e];
     }
     __syncthreads();
-    for (int e = tid; e < D * 2 * CH; e += blockDim.x) {
-        const int dd = e / (2 * CH), m = e - dd * (2 * CH);
+    for (int e = tid; e < D * NC; e += blockDim.x) {
+        const int dd = e / NC, m = e - dd * NC;
         ct[dd][m] = (m < ceff) ? QStore<T>::get(&qs[((m * n) / ceff) * QS + dd]) : 0.0;
     }
     __syncthreads();
 
     const int i = tid & (kQueryBlock - 1);
-    const int half = tid >> 7;
+    const int hd = tid >> 7;
     for (int it = 0; it < iters; ++it) {
-        // Distances of query i to clusters half*CH .. +CH-1.
+        // |c_m|^2: 16 lanes per cluster slot, a fixed-order lane reduction.
+        if (tid < NC * 16) {
+            const int m = tid >> 4, sub = tid & 15;
+            double a = 0.0;
+            for (int dd = sub; dd < D; dd += 16) a = fma(ct[dd][m], ct[dd][m], a);
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+            if (sub == 0) cc[m] = a;
+        }
+        // q_i . c_m over channel half hd, for every cluster slot.
+        double dot[NC];
+#pragma unroll
+        for (int m = 0; m < NC; ++m) dot[m] = 0.0;
         if (i < n) {
-            double acc[CH];
-#pragma unroll
-            for (int m = 0; m < CH; ++m) acc[m] = 0.0;
-            const T* qi = qs + i * QS;
+            const T* qi = qs + i * QS + hd * DH;
 #pragma unroll 4
-            for (int dd = 0; dd < D; ++dd) {
+            for (int dd = 0; dd < DH; ++dd) {
                 const double qv = QStore<T>::get(qi + dd);
-                const double* cr = &ct[dd][half * CH];
+                const double* cr = &ct[hd * DH + dd][0];
 #pragma unroll
-                for (int m = 0; m < CH; ++m) {
-                    const double df = qv - cr[m];
-                    acc[m] = fma(df, df, acc[m]);
-                }
+                for (int m = 0; m < NC; ++m) dot[m] = fma(qv, cr[m], dot[m]);
             }
-            double best = 0.0;
-            int bm = -1;
+            if (hd == 1) {
 #pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                const int mm = half * CH + m;
-                if (mm < ceff && (bm < 0 || acc[m] < best)) { best = acc[m]; bm = mm; }
+                for (int m = 0; m < NC; ++m) part[m][i] = dot[m];
             }
-            bdist[half][i] = best;
-            bidx[half][i] = bm;
         }
         __syncthreads();
-        // Combine the halves (ties to the smaller index) and rank members.
+        // Nearest centroid (ties to the smaller index) and member ranks.
         if (tid < kQueryBlock) {
             int a = -1;
             if (tid < n) {
-                a = bidx[0][tid];
-                const int m1 = bidx[1][tid];
-                if (m1 >= 0 && (a < 0 || bdist[1][tid] < bdist[0][tid])) a = m1;
+                double best = 0.0;
+#pragma unroll
+                for (int m = 0; m < NC; ++m) {
+                    const double dist = cc[m] - 2.0 * (dot[m] + part[m][tid]);
+                    if (m < ceff && (a < 0 || dist < best)) { best = dist; a = m; }
+                }
                 assign[tid] = a;
             }
             int rank = 0;
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
                 if (a == m) rank = __popcll(b & ((1ull << lane) - 1ull));
                 if (lane == 0) wcnt[wave][m] = __popcll(b);
             }
-            bdist[0][tid] = static_cast<double>(rank);      // reuse as scratch
+            rank_in_wave[tid] = rank;
         }
         __syncthreads();
         if (tid == 0) {
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
         __syncthreads();
         if (tid < n) {
             const int a = assign[tid];
-            const int pos = offs[a] + (tid >= 64 ? wcnt[0][a] : 0) + static_cast<int>(bdist[0][tid]);
+            const int pos = offs[a] + (tid >= 64 ? wcnt[0][a] : 0) + rank_in_wave[tid];
             members[pos] = tid;
         }
         __syncthreads();
@@ -214,10 +223,16 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
             const int m = e / D, dd = e - m * D;
             const int cnt = counts[m];
             if (cnt) {
+                // four independent partial sums (the sum is exact in any order)
                 const int* mem = members + offs[m];
-                double sum = 0.0;
-                for (int k = 0; k < cnt; ++k) sum += QStore<T>::get(&qs[mem[k] * QS + dd]);
-                ct[dd][m] = sum / static_cast<double>(cnt);
+                double s4[4] = {0.0, 0.0, 0.0, 0.0};
+                int k = 0;
+                for (; k + 4 <= cnt; k += 4) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) s4[u] += QStore<T>::get(&qs[mem[k + u] * QS + dd]);
+                }
+                for (; k < cnt; ++k) s4[0] += QStore<T>::get(&qs[mem[k] * QS + dd]);
+                ct[dd][m] = ((s4[0] + s4[1]) + (s4[2] + s4[3])) / static_cast<double>(cnt);
             }
         }
         __syncthreads();
