@@ -876,28 +876,31 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
 }
 
 // Fill the CSR row from the keep mask: ascending kept block indices, fp32
-// log-weights -ln p (+0 for p = 1), and p. Thread t owns keep-mask word t of
-// a 256-word chunk; an exclusive scan of the words' popcounts gives each
-// thread the position of its first kept block.
+// log-weights -ln p (+0 for p = 1), and p. The row's mask words are taken in
+// chunks of 256: thread t first counts word t of the chunk and a block-wide
+// exclusive scan gives every word's first output position (in LDS); then
+// each wave expands 64 of the chunk's words one at a time, lane l handling
+// bit l, so a word's kept blocks are written by consecutive lanes to
+// consecutive positions (v_mbcnt gives each lane its rank in the word).
 __global__ __launch_bounds__(256) void sip_fill_kernel(
     const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
     const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
     const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
     double* __restrict__ p_out) {
     __shared__ int wtot[4];
+    __shared__ int word_pos[256];
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
-    const int64_t words = (M + 63) / 64;
-    const uint64_t* cm = capmask + row * words;
-    const uint64_t* km = keepmask + row * words;
+    const int words = static_cast<int>((M + 63) / 64);
+    const uint64_t* cm = capmask + row * static_cast<int64_t>(words);
+    const uint64_t* km = keepmask + row * static_cast<int64_t>(words);
     const SipRow ri = rowinfo[row];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int64_t pos = rowptr[row];
-    for (int64_t base = 0; base < words; base += 256) {
-        const int64_t w = base + tid;
-        const uint64_t kw = (w < words) ? km[w] : 0ull;
-        const uint64_t cw = (w < words) ? cm[w] : 0ull;
-        const int pc = __popcll(kw);
+    for (int base = 0; base < words; base += 256) {
+        const int w = base + tid;
+        const int pc = (w < words) ? __popcll(km[w]) : 0;
         int incl = pc;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -911,18 +914,25 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
             if (k < wave) woff += wtot[k];
             tot += wtot[k];
         }
-        int64_t at = pos + woff + incl - pc;
-        uint64_t bits = kw;
-        while (bits) {
-            const int bit = __ffsll(static_cast<long long>(bits)) - 1;
-            bits &= bits - 1;
-            const int64_t j = w * 64 + bit;
-            const bool capped = (cw >> bit) & 1ull;
-            const double p = capped ? 1.0 : sip_p(false, ri, sg[j]);
-            idx[at] = static_cast<int32_t>(j);
-            logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
-            p_out[at] = p;
-            ++at;
+        word_pos[tid] = woff + incl - pc;
+        __syncthreads();
+        const int wend = min(64, words - base - 64 * wave);
+        for (int u = 0; u < wend; ++u) {
+            const int wl = 64 * wave + u;                 // word within the chunk
+            const uint64_t kw = km[base + wl];            // wave-uniform
+            if (kw == 0) continue;
+            const uint64_t cw = cm[base + wl];
+            if ((kw >> lane) & 1ull) {
+                const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(kw >> 32),
+                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(kw), 0));
+                const int64_t at = pos + word_pos[wl] + rank;
+                const int64_t j = static_cast<int64_t>(base + wl) * 64 + lane;
+                const bool capped = (cw >> lane) & 1ull;
+                const double p = capped ? 1.0 : sip_p(false, ri, sg[j]);
+                idx[at] = static_cast<int32_t>(j);
+                logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
+                p_out[at] = p;
+            }
         }
         pos += tot;
         __syncthreads();
