@@ -50,6 +50,10 @@ def parse():
                     help="target length of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--reuse-sweep", action="store_true",
+                    help="plan-reuse report instead of the benchmark line: small video-shaped "
+                         "layer, plan built at step 0, attention at steps 0-3 on drifting "
+                         "Q/K/V, budgets 5/10/20%%; time and error against dense per step")
     return ap.parse_args()
 
 
@@ -130,8 +134,69 @@ def cpu_baseline(q, k, v, budget, seed, seconds):
     return layer_s, done, elapsed, threads
 
 
+def reuse_sweep():
+    """[hamidun, kernel paragraph]: a plan is rebuilt every 4 denoising steps
+    and reused in between. Builds the plan at step 0 on the small
+    video-shaped layer and runs the sparse and the dense kernel at steps 0-3,
+    Q/K/V drifting by 0.05 N(0,1) per step; prints one JSON object."""
+    import torch
+    import sampled_block_sparse_amd as absa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q0, k0, v0 = synth.make_inputs("small")
+    B, H, N, d = (int(x) for x in q0.shape)
+    M = N // 4
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        fn()
+        ms = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    rows = []
+    for pct in (5, 10, 20):
+        budget = synth.budget_blocks(pct, M)
+        q, k, v = q0, k0, v0
+        qd, kd = q.to(dev), k.to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        plan = absa.absa_plan_create(qd, kd, budget, synth.sip_seed(0))
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        for step in range(synth.REUSE_STEPS):
+            if step:
+                q, k, v = (synth.drift(x, seed=100 * step + i) for i, x in enumerate((q, k, v)))
+            qd, kd, vd = (x.to(dev) for x in (q, k, v))
+            out = torch.empty_like(qd)
+            dense = torch.empty_like(qd)
+            sparse_ms = timed(lambda: absa.absa_sparse_attention(plan, qd, kd, vd, out))
+            dense_ms = timed(lambda: absa.absa_dense_attention(qd, kd, vd, dense))
+            diff = (out.float() - dense.float())
+            rows.append({
+                "budget_pct": pct, "budget_blocks": budget, "step": step,
+                "plan_built_at_step": 0, "plan_ms": round(plan_ms, 3) if step == 0 else None,
+                "sparse_attn_ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+                "rel_l2_vs_dense": float(diff.norm() / dense.float().norm()),
+                "max_abs_vs_dense": float(diff.abs().max()),
+            })
+        plan.destroy()
+    print(json.dumps({"mode": "reuse_sweep", "workload": WORKLOADS["small"],
+                      "drift": "Q/K/V += 0.05 N(0,1) per step", "rows": rows}))
+
+
 def main():
     args = parse()
+    if args.reuse_sweep:
+        reuse_sweep()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
