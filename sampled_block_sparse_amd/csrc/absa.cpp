@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <string>
@@ -60,6 +61,7 @@ absa_status hip_fail(hipError_t e, const char* what) {
         hipError_t e_ = (call);                            \
         if (e_ != hipSuccess) return hip_fail(e_, (what)); \
     } while (0)
+#define ABSA_HIP_RET(call, what) ABSA_HIP(call, what)
 
 // Allocation failure can be forced for tests: ABSA_FAULT_INJECT=alloc.
 bool inject_alloc_failure() {
@@ -150,6 +152,100 @@ struct DeviceArena {
     }
 };
 
+// Bump allocator over one device block, for a plan build's temporaries.
+// With base == nullptr it only measures (every pointer stays null).
+struct Carve {
+    char* base = nullptr;
+    size_t cap = 0, used = 0;
+    template <typename T>
+    absa_status alloc(T** out, int64_t count, const char* what) {
+        *out = nullptr;
+        if (count <= 0) return ABSA_OK;
+        if (inject_alloc_failure())
+            return fail(ABSA_ERR_OUT_OF_MEMORY, "%s: allocation failure injected", what);
+        const size_t bytes = (static_cast<size_t>(count) * sizeof(T) + 255) & ~size_t(255);
+        if (base) {
+            if (used + bytes > cap) return fail(ABSA_ERR_DEVICE, "%s: workspace overflow", what);
+            *out = reinterpret_cast<T*>(base + used);
+        }
+        used += bytes;
+        return ABSA_OK;
+    }
+};
+
+// Per-device plan-building workspace: one block that successive plan builds
+// on a device reuse for their temporaries (it grows to the largest build).
+// A build holds it for its whole (synchronous) duration; a build that finds
+// it held by another thread allocates a block of its own.
+struct Workspace {
+    std::mutex busy;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<std::unique_ptr<Workspace>> g_ws;
+
+Workspace* device_workspace(int dev) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (static_cast<size_t>(dev) >= g_ws.size()) g_ws.resize(dev + 1);
+    if (!g_ws[dev]) g_ws[dev].reset(new Workspace());
+    return g_ws[dev].get();
+}
+
+// A build's hold on a workspace block of at least `bytes` bytes.
+class WorkspaceLease {
+  public:
+    explicit WorkspaceLease(hipStream_t s) : s_(s) {}
+    // Work queued on the block may still be running when a build fails
+    // part-way: wait for the stream before another build can take the block.
+    ~WorkspaceLease() {
+        if (lock_.owns_lock()) (void)hipStreamSynchronize(s_);
+        if (own_) (void)hipFreeAsync(own_, s_);
+    }
+    absa_status acquire(size_t bytes, char** out) {
+        *out = nullptr;
+        if (bytes == 0) return ABSA_OK;
+        int dev = 0;
+        ABSA_HIP_RET(hipGetDevice(&dev), "current device");
+        Workspace* ws = device_workspace(dev);
+        lock_ = std::unique_lock<std::mutex>(ws->busy, std::try_to_lock);
+        if (lock_.owns_lock()) {
+            if (ws->bytes < bytes) {
+                if (ws->ptr) (void)hipFreeAsync(ws->ptr, s_);
+                ws->ptr = nullptr;
+                ws->bytes = 0;
+                ABSA_HIP_RET(pool_alloc(&ws->ptr, bytes, s_), "plan workspace");
+                ws->bytes = bytes;
+            }
+            *out = static_cast<char*>(ws->ptr);
+        } else {
+            ABSA_HIP_RET(pool_alloc(&own_, bytes, s_), "plan workspace");
+            *out = static_cast<char*>(own_);
+        }
+        return ABSA_OK;
+    }
+
+  private:
+    hipStream_t s_;
+    void* own_ = nullptr;
+    std::unique_lock<std::mutex> lock_;
+};
+
+// Temporaries of a plan build (null when not needed).
+struct PlanTemps {
+    float* kbar = nullptr;
+    uint16_t* kbar3 = nullptr;
+    float* cent = nullptr;
+    float* w = nullptr;
+    float* scores = nullptr;
+    float2* part = nullptr;
+    uint64_t* capmask = nullptr;
+    uint64_t* keepmask = nullptr;
+    SipRow* rowinfo = nullptr;
+    int64_t* counts = nullptr;
+    PlanStatus* status = nullptr;
+};
+
 #define ABSA_TRY(expr)                       \
     do {                                     \
         absa_status s_ = (expr);             \
@@ -185,31 +281,35 @@ void fill_dims(absa_plan_s* p, int64_t B, int64_t H, int64_t N, int64_t d) {
     p->rows = B * H * p->QB;
 }
 
-// SIP on device scores, shared by plan_create and plan_from_scores. Fills
-// rowptr/idx/logw/p of plan (allocated in arena). One device-to-host read of
-// the total count and the score check flag, then the fill kernel.
-absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_t seed,
-                    hipStream_t s, DeviceArena& arena) {
+// Temporaries of the SIP stage (masks, per-row outcome, counts, status).
+template <typename A>
+absa_status sip_temps(A& a, const absa_plan_s* P, PlanTemps& t) {
     const int64_t rows = P->rows;
     const int64_t words = (P->M + 63) / 64;
-    uint64_t* capmask = nullptr;
-    uint64_t* keepmask = nullptr;
-    SipRow* rowinfo = nullptr;
-    int64_t* counts = nullptr;
-    PlanStatus* status = nullptr;
-    ABSA_TRY(arena.alloc(&capmask, rows * words, "cap mask"));
-    ABSA_TRY(arena.alloc(&keepmask, rows * words, "keep mask"));
-    ABSA_TRY(arena.alloc(&rowinfo, rows, "row info"));
-    ABSA_TRY(arena.alloc(&counts, rows, "row counts"));
-    ABSA_TRY(arena.alloc(&status, 1, "plan status"));
+    ABSA_TRY(a.alloc(&t.capmask, rows * words, "cap mask"));
+    ABSA_TRY(a.alloc(&t.keepmask, rows * words, "keep mask"));
+    ABSA_TRY(a.alloc(&t.rowinfo, rows, "row info"));
+    ABSA_TRY(a.alloc(&t.counts, rows, "row counts"));
+    ABSA_TRY(a.alloc(&t.status, 1, "plan status"));
+    return ABSA_OK;
+}
+
+// SIP on device scores, shared by plan_create and plan_from_scores. Fills
+// rowptr/idx/logw/p of the plan (allocated in arena, owned by the plan)
+// using the temporaries in t. One device-to-host read of the total count and
+// the score check flag, then the fill kernel. Returns with the fill queued;
+// the caller synchronises.
+absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_t seed,
+                    hipStream_t s, DeviceArena& arena, const PlanTemps& t) {
+    const int64_t rows = P->rows;
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
-    ABSA_HIP(hipMemsetAsync(status, 0, sizeof(PlanStatus), s), "clear plan status");
-    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, capmask, keepmask,
-                              rowinfo, counts, status, s),
+    ABSA_HIP(hipMemsetAsync(t.status, 0, sizeof(PlanStatus), s), "clear plan status");
+    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, t.capmask,
+                              t.keepmask, t.rowinfo, t.counts, t.status, s),
              "SIP count kernel");
-    ABSA_HIP(launch_scan(counts, rows, P->rowptr, status, s), "row scan kernel");
+    ABSA_HIP(launch_scan(t.counts, rows, P->rowptr, t.status, s), "row scan kernel");
     PlanStatus host{};
-    ABSA_HIP(hipMemcpyAsync(&host, status, sizeof(PlanStatus), hipMemcpyDeviceToHost, s),
+    ABSA_HIP(hipMemcpyAsync(&host, t.status, sizeof(PlanStatus), hipMemcpyDeviceToHost, s),
              "read plan size");
     ABSA_HIP(hipStreamSynchronize(s), "plan synchronisation");
     if (host.bad_scores)
@@ -220,11 +320,10 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
     ABSA_TRY(arena.alloc(&P->logw, P->nnz, "plan log-weights"));
     ABSA_TRY(arena.alloc(&P->p, P->nnz, "plan probabilities"));
     if (P->nnz > 0) {
-        ABSA_HIP(launch_sip_fill(scores, rows, P->M, capmask, keepmask, rowinfo, P->rowptr,
+        ABSA_HIP(launch_sip_fill(scores, rows, P->M, t.capmask, t.keepmask, t.rowinfo, P->rowptr,
                                  P->idx, P->logw, P->p, s),
                  "SIP fill kernel");
     }
-    ABSA_HIP(hipStreamSynchronize(s), "plan completion");
     return ABSA_OK;
 }
 
@@ -308,33 +407,51 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     const int C = params->n_clusters;
     const Dtype dt = (dtype == ABSA_BF16) ? kBF16 : kF32;
 
+    const bool keep_inter = params->keep_intermediates != 0;
     absa_status st = [&]() -> absa_status {
         ABSA_TRY(set_plan_device(P));
+        // Temporaries come from the device's reusable workspace; the plan's
+        // own buffers (and the intermediates it keeps) from the pool.
+        auto temps = [&](auto& a, PlanTemps& t) -> absa_status {
+            if (!keep_inter) {
+                ABSA_TRY(a.alloc(&t.kbar, B * H * M * d, "mean keys"));
+                ABSA_TRY(a.alloc(&t.cent, P->rows * C * d, "centroids"));
+                ABSA_TRY(a.alloc(&t.w, P->rows * C, "cluster weights"));
+                ABSA_TRY(a.alloc(&t.scores, P->rows * M, "scores"));
+            }
+            ABSA_TRY(a.alloc(&t.kbar3, B * H * M * 3 * d, "split mean keys"));
+            ABSA_TRY(a.alloc(&t.part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
+            return sip_temps(a, P, t);
+        };
+        PlanTemps t;
+        Carve measure;
+        ABSA_TRY(temps(measure, t));
+        WorkspaceLease lease(s);
+        Carve carve;
+        ABSA_TRY(lease.acquire(measure.used, &carve.base));
+        carve.cap = measure.used;
+        ABSA_TRY(temps(carve, t));
         DeviceArena arena(s);
-        uint16_t* kbar3 = nullptr;
-        ABSA_TRY(arena.alloc(&P->kbar, B * H * M * d, "mean keys"));
-        ABSA_TRY(arena.alloc(&kbar3, B * H * M * 3 * d, "split mean keys"));
-        ABSA_TRY(arena.alloc(&P->cent, P->rows * C * d, "centroids"));
-        ABSA_TRY(arena.alloc(&P->w, P->rows * C, "cluster weights"));
-        ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
-        float2* part = nullptr;
-        ABSA_TRY(arena.alloc(&part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
-        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), P->kbar, kbar3, s),
+        if (keep_inter) {
+            ABSA_TRY(arena.alloc(&P->kbar, B * H * M * d, "mean keys"));
+            ABSA_TRY(arena.alloc(&P->cent, P->rows * C * d, "centroids"));
+            ABSA_TRY(arena.alloc(&P->w, P->rows * C, "cluster weights"));
+            ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
+            t.kbar = P->kbar; t.cent = P->cent; t.w = P->w; t.scores = P->scores;
+        }
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kbar3, s),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
-                               P->cent, P->w, s),
+                               t.cent, t.w, s),
                  "k-means kernel");
-        ABSA_HIP(launch_scores(P->cent, P->w, kbar3, B * H, P->QB, M, static_cast<int>(d), C,
-                               part, P->scores, s),
+        ABSA_HIP(launch_scores(t.cent, t.w, t.kbar3, B * H, P->QB, M, static_cast<int>(d), C,
+                               t.part, t.scores, s),
                  "score kernel");
-        ABSA_TRY(run_sip(P, P->scores, params->budget_blocks, params->seed, s, arena));
+        ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, s, arena, t));
         keep(arena, P);
-        if (!params->keep_intermediates) {
-            float* tmp[] = {P->kbar, P->cent, P->w, P->scores};
-            for (float* b : tmp)
-                if (b) (void)hipFreeAsync(b, s);
-            P->kbar = P->cent = P->w = P->scores = nullptr;
-        }
+        // the workspace is released (and may be reused) only once the build
+        // has finished on the device
+        ABSA_HIP(hipStreamSynchronize(s), "plan completion");
         return ABSA_OK;
     }();
     if (st != ABSA_OK) {
@@ -364,9 +481,18 @@ absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
     fill_dims(P, B, H, N, d);
     absa_status st = [&]() -> absa_status {
         ABSA_TRY(set_plan_device(P));
+        PlanTemps t;
+        Carve measure;
+        ABSA_TRY(sip_temps(measure, P, t));
+        WorkspaceLease lease(s);
+        Carve carve;
+        ABSA_TRY(lease.acquire(measure.used, &carve.base));
+        carve.cap = measure.used;
+        ABSA_TRY(sip_temps(carve, P, t));
         DeviceArena arena(s);
-        ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, s, arena));
+        ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, s, arena, t));
         keep(arena, P);
+        ABSA_HIP(hipStreamSynchronize(s), "plan completion");
         return ABSA_OK;
     }();
     if (st != ABSA_OK) {
@@ -570,6 +696,16 @@ absa_status absa_release_cached_memory(void) {
     ABSA_HIP(device_pool(dev, false, &pool), "library memory pool");
     if (!pool) return ABSA_OK;
     ABSA_HIP(hipDeviceSynchronize(), "device synchronisation");
+    {
+        Workspace* ws = device_workspace(dev);
+        std::unique_lock<std::mutex> lock(ws->busy, std::try_to_lock);
+        if (lock.owns_lock() && ws->ptr) {
+            ABSA_HIP(hipFreeAsync(ws->ptr, nullptr), "free the plan workspace");
+            ws->ptr = nullptr;
+            ws->bytes = 0;
+            ABSA_HIP(hipDeviceSynchronize(), "device synchronisation");
+        }
+    }
     ABSA_HIP(hipMemPoolTrimTo(pool, 0), "trim the library memory pool");
     return ABSA_OK;
 }
