@@ -172,12 +172,15 @@ absa_status absa_dense_attention(const void* q, const void* k, const void* v, vo
  * device (see absa_release_cached_memory). */
 void absa_plan_destroy(absa_plan plan);
 
-/* The library allocates plans and the temporaries of plan building from one
- * stream-ordered memory pool per device, which keeps freed memory for the
- * next plan instead of returning it to the driver (about 3.6 GB at
- * B=1, H=40, N=75,600, d=128). This call waits for the current device to go
- * idle and returns all of that device's cached, unused pool memory to the
- * system; live plans keep theirs. ABSA_ERR_DEVICE on a HIP failure. */
+/* The library allocates plans from one stream-ordered memory pool per
+ * device, which keeps freed memory for the next plan instead of returning it
+ * to the driver, and keeps one plan-building workspace per device for the
+ * temporaries of absa_plan_create / absa_plan_from_scores (it grows to the
+ * largest build: about 2.9 GB at B=1, H=40, N=75,600, d=128). This call
+ * waits for the current device to go idle, frees that device's workspace
+ * (unless a build on another thread holds it) and returns all cached, unused
+ * pool memory to the system; live plans keep theirs. ABSA_ERR_DEVICE on a
+ * HIP failure. */
 absa_status absa_release_cached_memory(void);
 
 /* Static name of a status code. */
