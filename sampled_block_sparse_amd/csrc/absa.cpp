@@ -234,7 +234,8 @@ class WorkspaceLease {
 // Temporaries of a plan build (null when not needed).
 struct PlanTemps {
     float* kbar = nullptr;
-    uint16_t* kbar3 = nullptr;
+    int8_t* kq = nullptr;
+    int* kx = nullptr;
     float* cent = nullptr;
     float* w = nullptr;
     float* scores = nullptr;
@@ -419,7 +420,8 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
                 ABSA_TRY(a.alloc(&t.w, P->rows * C, "cluster weights"));
                 ABSA_TRY(a.alloc(&t.scores, P->rows * M, "scores"));
             }
-            ABSA_TRY(a.alloc(&t.kbar3, B * H * M * 3 * d, "split mean keys"));
+            ABSA_TRY(a.alloc(&t.kq, B * H * M * 3 * d, "mean-key digits"));
+            ABSA_TRY(a.alloc(&t.kx, B * H * M, "mean-key exponents"));
             ABSA_TRY(a.alloc(&t.part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
             return sip_temps(a, P, t);
         };
@@ -439,12 +441,12 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
             ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
             t.kbar = P->kbar; t.cent = P->cent; t.w = P->w; t.scores = P->scores;
         }
-        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kbar3, s),
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kq, t.kx, s),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
                                t.cent, t.w, s),
                  "k-means kernel");
-        ABSA_HIP(launch_scores(t.cent, t.w, t.kbar3, B * H, P->QB, M, static_cast<int>(d), C,
+        ABSA_HIP(launch_scores(t.cent, t.w, t.kq, t.kx, B * H, P->QB, M, static_cast<int>(d), C,
                                t.part, t.scores, s),
                  "score kernel");
         ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, s, arena, t));

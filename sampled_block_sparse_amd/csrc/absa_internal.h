@@ -34,10 +34,11 @@ struct PlanStatus {
     int32_t pad;
 };
 
-// kbar: fp32 means [BH, M, d]; kbar3: their exact three-way bf16 split
-// [BH, M, 3, d] (hi, mid, lo planes), the score kernel's operand.
+// kbar: fp32 means [BH, M, d]; kq: their block floating point int8 digits
+// [BH, M, 3, d] (planes X2, X1, X0) and kx: the exponent of each mean [BH, M],
+// the score kernel's operand.
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, uint16_t* kbar3, hipStream_t s);
+                            float* kbar, int8_t* kq, int* kx, hipStream_t s);
 
 hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
                          int C, int iters, float* cent, float* w, hipStream_t s);
@@ -46,7 +47,7 @@ hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
 // argument of launch_scores).
 int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C);
 
-hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3,
+hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
                          int64_t BH, int64_t QB, int64_t M, int d, int C,
                          float2* part, float* scores, hipStream_t s);
 

@@ -28,37 +28,48 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Split of an fp32 value into three bf16 values hi + mid + lo == x (exact for
-// normal x: each step removes the 8 leading significant bits, and the
-// subtractions are exact).
+// Block floating point for the score contraction. A vector x of fp32 values
+// with a shared exponent e (every |x_i| < 2^e, e from frexp of the largest
+// |x_i|) is represented as integers X_i = rint(x_i 2^(22-e)), |X_i| <= 2^22,
+// each split into balanced base-256 digits X = X2 2^16 + X1 2^8 + X0 with
+// X1, X0 in [-128, 127] and X2 in [-64, 64], all int8. Rounding to X costs
+// at most 2^(e-23) per element.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-    const __bf16 h = static_cast<__bf16>(x);
-    const float r1 = x - static_cast<float>(h);
-    const __bf16 m = static_cast<__bf16>(r1);
-    const float r2 = r1 - static_cast<float>(m);
-    const __bf16 l = static_cast<__bf16>(r2);
-    hi = __builtin_bit_cast(uint16_t, h);
-    mid = __builtin_bit_cast(uint16_t, m);
-    lo = __builtin_bit_cast(uint16_t, l);
+__device__ __forceinline__ int bfp_exponent(float amax) {
+    int e = 0;
+    (void)frexpf(amax, &e);
+    return e;
+}
+__device__ __forceinline__ void bfp_digits(float x, int e, int8_t& d2, int8_t& d1, int8_t& d0) {
+    const int X = static_cast<int>(rintf(ldexpf(x, 22 - e)));
+    const int x0 = ((X + 128) & 255) - 128;
+    const int r = (X - x0) >> 8;
+    const int x1 = ((r + 128) & 255) - 128;
+    d0 = static_cast<int8_t>(x0);
+    d1 = static_cast<int8_t>(x1);
+    d2 = static_cast<int8_t>((r - x1) >> 8);
 }
 
 // ---------------------------------------------------------------------------
 // Mean keys [hamidun, IBCS paragraph: "averaged keys"]:
 // kbar[bh, j, :] = (k[bh, 4j] + k[bh, 4j+1] + k[bh, 4j+2] + k[bh, 4j+3]) / 4.
-// One thread per (bh, j, 4-channel chunk); the fp32 sum of four bf16 values
-// is exact unless their exponents differ by more than 15. Also writes the
-// three-way bf16 split of each mean, kbar3[bh, j, plane, :], the operand of
-// the score kernel's matrix products.
+// One thread per (bh, j, 4-channel chunk), a KV block's d/4 threads in
+// consecutive lanes; the fp32 sum of four bf16 values is exact unless their
+// exponents differ by more than 15. Also writes each mean's block floating
+// point form, the operand of the score kernel's matrix products: digit
+// planes kq[bh, j, plane, :] (plane 0 = X2) and the exponent kx[bh, j].
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kbar,
-                                 uint16_t* __restrict__ kbar3, int64_t chunks, int d) {
+__global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
+                                                        float* __restrict__ kbar,
+                                                        int8_t* __restrict__ kq,
+                                                        int* __restrict__ kx, int64_t chunks,
+                                                        int d) {
     const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (c >= chunks) return;
-    const int per_row = d >> 2;
-    const int64_t blk = c / per_row;            // flattened bh*M + j
-    const int d0 = static_cast<int>(c - blk * per_row) << 2;
+    const bool ok = c < chunks;
+    const int per_row = d >> 2;                 // 16 or 32 lanes per KV block
+    const int64_t blk = (ok ? c : chunks - 1) / per_row;            // flattened bh*M + j
+    const int d0 = static_cast<int>((ok ? c : chunks - 1) - blk * per_row) << 2;
     const T* src = k + (blk * kKvBlock) * d + d0;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -68,16 +79,23 @@ __global__ void mean_keys_kernel(const T* __restrict__ k, float* __restrict__ kb
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= 0.25f;
+    // shared exponent of the block's d channels (its lanes are consecutive)
+    float amax = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
+    for (int off = 1; off < per_row; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (!ok) return;
     *reinterpret_cast<float4*>(kbar + blk * d + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    uint16_t pl[3][4];
+    const int ex = bfp_exponent(amax);
+    int8_t pl[3][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) split3_bf16(acc[e], pl[0][e], pl[1][e], pl[2][e]);
-    uint16_t* dst = kbar3 + blk * 3 * d + d0;
+    for (int e = 0; e < 4; ++e) bfp_digits(acc[e], ex, pl[0][e], pl[1][e], pl[2][e]);
+    int8_t* dst = kq + blk * 3 * d + d0;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<uint2*>(dst + q * d) =
-            make_uint2(pl[q][0] | (static_cast<uint32_t>(pl[q][1]) << 16),
-                       pl[q][2] | (static_cast<uint32_t>(pl[q][3]) << 16));
+        *reinterpret_cast<uint32_t*>(dst + q * d) =
+            static_cast<uint8_t>(pl[q][0]) | (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][1])) << 8) |
+            (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][2])) << 16) |
+            (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][3])) << 24);
+    if (d0 == 0) kx[blk] = ex;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,18 +272,19 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // IBCS scores [hamidun, IBCS paragraph]: for each query block r and KV block
 // j, s_j = sum_m w_m * softmax_j(c_m . kbar_j / sqrt(d)), softmax over all M
 // KV blocks of the head. This is a dense contraction (centroids x mean keys,
-// per head) that must be fp32-accurate; it runs on the bf16 MFMA
-// (32x32x16) with both operands split three ways, c = c1 + c2 + c3 and
-// kbar = k1 + k2 + k3, summing the six products c1k1, c1k2, c2k1, c1k3,
-// c2k2, c3k1 (the three dropped ones are below 2^-24 of the result); each
-// bf16 product is exact in fp32 and accumulates in fp32, c1k1 in its own
-// accumulator. A wave owns 32 centroid slots (32/CP query blocks of CP
+// per head) that must be accurate to 1e-4 relative; it runs on the int8 MFMA
+// (32x32x32) on block floating point forms of both operands (three int8
+// digits per value, one exponent per centroid and per mean key), summing
+// the six digit products of weight >= 2^16 in int32 accumulators (exact)
+// and combining them in fp32; the result carries about 2^-21 of the dot
+// product's scale. A wave owns 32 centroid slots (32/CP query blocks of CP
 // slots; slots past C have weight 0) against 32-key tiles staged in LDS.
 // Pass 1 keeps per-lane running (max, sum) of each centroid's exponentials
 // and merges them across lanes; pass 2 recomputes the logits and writes the
 // weighted sum over the block's clusters. MFMA D layout (32x32): lane l
 // holds column l%32 (a key) and rows (i/4)*8 + (l/32)*4 + i%4 (centroid
-// slots) for i < 16.
+// slots) for i < 16; operand layout (int8, K = 32): lane l holds row l%32
+// of A and column l%32 of B at k = (l/32)*16 .. +16.
 // ---------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -282,18 +301,24 @@ constexpr int kScoreTile = 32;
 template <int CP, int D, bool PASS2>
 __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict__ cent,
                                                         const float* __restrict__ w,
-                                                        const uint16_t* __restrict__ kbar3,
+                                                        const int8_t* __restrict__ kq,
+                                                        const int* __restrict__ kx,
                                                         int64_t QB, int64_t M, int C,
                                                         int chunk_tiles, int nchunks,
                                                         float scale_log2,
                                                         float2* __restrict__ part,
                                                         float* __restrict__ scores) {
     constexpr int RPW = 32 / CP;                    // query blocks per wave
-    constexpr int NSTEP = D / 16;                   // MFMA k-steps
-    constexpr int KROW = 3 * D + 8;                 // LDS key row (bf16), padded
-    constexpr int CHUNKS = kScoreTile * 3 * D / 8;  // 16-byte pieces per tile
-    constexpr int CPT = CHUNKS / 256;               // per thread
-    __shared__ __align__(16) uint16_t ks[2][kScoreTile * KROW];
+    constexpr int NSTEP = D / 32;                   // MFMA k-steps (32 channels each)
+    constexpr int KROW = 3 * D + 16;                // LDS key row (bytes), padded
+    constexpr int CHUNKS = kScoreTile * 3 * D / 16; // 16-byte pieces per tile
+    constexpr int CPT = (CHUNKS + 255) / 256;       // per thread (last pass partial
+                                                    // when CHUNKS % 256 != 0; whole waves)
+    static_assert(CHUNKS % 64 == 0, "tile pieces must split over whole waves");
+    __shared__ __align__(16) int8_t ks[2][kScoreTile * KROW];
+    __shared__ float colf[2][kScoreTile];           // 2^(key exponent) of the tile's keys
+    __shared__ int slot_exp[kScoreWaves][32];       // centroid exponents, per wave
+    __shared__ __align__(16) float rowf_s[kScoreWaves][2][16];  // row factors, per half
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -308,32 +333,39 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     const int64_t t1 = (t0 + chunk_tiles < ntiles) ? t0 + chunk_tiles : ntiles;
 
     // A operands: this lane's centroid slot (row col of the 32x32 block),
-    // channels s*16 + half*8 .. +8 of each step, in three bf16 planes.
+    // channels s*32 + half*16 .. +16 of each step, as the three int8 digit
+    // planes of the centroid's block floating point form.
     const int64_t my_r = r0 + col / CP;
     const int my_m = col % CP;
     const bool slot_ok = (my_r < QB) && (my_m < C);
-    uint4 a1[NSTEP], a2[NSTEP], a3[NSTEP];
+    typedef int intx4 __attribute__((ext_vector_type(4)));
+    intx4 a2[NSTEP], a1[NSTEP], a0[NSTEP];
     {
         const float* src = cent + ((bh * QB + my_r) * C + my_m) * D;
+        float amax = 0.0f;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-            uint16_t hv[8], mv[8], lv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = slot_ok ? src[st * 16 + half * 8 + e] : 0.0f;
-                split3_bf16(x, hv[e], mv[e], lv[e]);
+            for (int e = 0; e < 16; ++e)
+                amax = fmaxf(amax, slot_ok ? fabsf(src[st * 32 + half * 16 + e]) : 0.0f);
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int ex = bfp_exponent(amax);
+        if (half == 0) slot_exp[wave][col] = ex;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            int8_t h2[16], h1[16], h0[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float x = slot_ok ? src[st * 32 + half * 16 + e] : 0.0f;
+                bfp_digits(x, ex, h2[e], h1[e], h0[e]);
             }
-            auto pack = [](const uint16_t (&v)[8]) {
-                return make_uint4(v[0] | (static_cast<uint32_t>(v[1]) << 16),
-                                  v[2] | (static_cast<uint32_t>(v[3]) << 16),
-                                  v[4] | (static_cast<uint32_t>(v[5]) << 16),
-                                  v[6] | (static_cast<uint32_t>(v[7]) << 16));
-            };
-            a1[st] = pack(hv);
-            a2[st] = pack(mv);
-            a3[st] = pack(lv);
+            __builtin_memcpy(&a2[st], h2, 16);
+            __builtin_memcpy(&a1[st], h1, 16);
+            __builtin_memcpy(&a0[st], h0, 16);
         }
     }
+    __syncthreads();
 
     // Accumulator row i of this lane is centroid slot (i/4)*8 + half*4 + i%4.
     auto slot_of = [&](int i) { return (i >> 2) * 8 + half * 4 + (i & 3); };
@@ -343,11 +375,18 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     auto part_index = [&](int slot) {
         return ((bh * QB + r0 + slot / CP) * C + slot % CP) * nchunks;
     };
+    // Per-row factor: the log2-domain scale times 2^(e_slot - 28) (the digit
+    // sums carry 2^(44 - e_c - e_k), and the combination below 2^-16).
+    // Kept in LDS (read once per tile) rather than in 16 registers.
+    if (col < 16) rowf_s[wave][half][col] = ldexpf(scale_log2, slot_exp[wave][slot_of(col)] - 28);
+    __syncthreads();
 
-    const uint16_t* kb = kbar3 + bh * M * 3 * D;
+    const int8_t* kb = kq + bh * M * 3 * D;
+    const int* kxb = kx + bh * M;
     // Native vectors (not uint4 structs): their copies stay in registers.
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 pre[CPT];
+    int pre_x = 0;
     // Tile loads are unconditional: a key index past M is clamped to M-1 and
     // its logits are never used, so the loop carries no divergent load.
     auto fetch_tile = [&](int64_t t) __attribute__((always_inline)) {
@@ -355,43 +394,55 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int e = tid + 256 * i;
-            const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
-            const int64_t j = (j0 + key < M) ? j0 + key : M - 1;
-            pre[i] = *reinterpret_cast<const u32x4*>(kb + j * 3 * D + c8 * 8);
+            if (CHUNKS % 256 == 0 || e < CHUNKS) {
+                const int key = e / (3 * D / 16), c16 = e - key * (3 * D / 16);
+                const int64_t j = (j0 + key < M) ? j0 + key : M - 1;
+                pre[i] = *reinterpret_cast<const u32x4*>(kb + j * 3 * D + c16 * 16);
+            }
         }
+        if (tid < kScoreTile) pre_x = kxb[(j0 + tid < M) ? j0 + tid : M - 1];
     };
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int e = tid + 256 * i;
-            const int key = e / (3 * D / 8), c8 = e - key * (3 * D / 8);
-            *reinterpret_cast<u32x4*>(&ks[buf][key * KROW + c8 * 8]) = pre[i];
+            if (CHUNKS % 256 == 0 || e < CHUNKS) {
+                const int key = e / (3 * D / 16), c16 = e - key * (3 * D / 16);
+                *reinterpret_cast<u32x4*>(&ks[buf][key * KROW + c16 * 16]) = pre[i];
+            }
         }
+        if (tid < kScoreTile) colf[buf][tid] = __int_as_float((pre_x + 127) << 23);
     };
-    auto as8 = [](uint4 u) { return __builtin_bit_cast(bf16x8, u); };
+    // Scaled logits of the tile: the six digit products of weight >= 2^16
+    // (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2) on the int8 MFMA, combined in
+    // fp32 as 2^16 P22 + 2^8 P21 + P20, times the row and column factors.
+    // The dropped products are below 2^-21 of the dot product's scale.
     auto tile_logits = [&](int buf) __attribute__((always_inline)) {
-        floatx16 acc, acc2;
-        const uint16_t* kr = &ks[buf][col * KROW + half * 8];
+        typedef int intx16 __attribute__((ext_vector_type(16)));
+        intx16 p22 = {}, p21 = {}, p20 = {};
+        const int8_t* kr = &ks[buf][col * KROW + half * 16];
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-            const bf16x8 b1 = as8(*reinterpret_cast<const uint4*>(kr + st * 16));
-            const bf16x8 b2 = as8(*reinterpret_cast<const uint4*>(kr + D + st * 16));
-            const bf16x8 b3 = as8(*reinterpret_cast<const uint4*>(kr + 2 * D + st * 16));
-            if (st == 0) {
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, floatx16{}, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, floatx16{}, 0, 0, 0);
-            } else {
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b1, acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a3[st]), b1, acc2, 0, 0, 0);
-            }
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b2, acc2, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b3, acc2, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a2[st]), b1, acc2, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(a1[st]), b2, acc2, 0, 0, 0);
+            const intx4 b2 = *reinterpret_cast<const intx4*>(kr + st * 32);
+            const intx4 b1 = *reinterpret_cast<const intx4*>(kr + D + st * 32);
+            const intx4 b0 = *reinterpret_cast<const intx4*>(kr + 2 * D + st * 32);
+            p22 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b2, p22, 0, 0, 0);
+            p21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b1, p21, 0, 0, 0);
+            p21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b2, p21, 0, 0, 0);
+            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b0, p20, 0, 0, 0);
+            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b1, p20, 0, 0, 0);
+            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[st], b2, p20, 0, 0, 0);
         }
+        const float cf = colf[buf][col];
+        const floatx16 rowf = *reinterpret_cast<const floatx16*>(&rowf_s[wave][half][0]);
+        floatx16 x;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += acc2[i];
-        return acc;
+        for (int i = 0; i < 16; ++i) {
+            const float t = fmaf(static_cast<float>(p22[i]), 65536.0f,
+                                 fmaf(static_cast<float>(p21[i]), 256.0f, static_cast<float>(p20[i])));
+            x[i] = (t * rowf[i]) * cf;
+        }
+        return x;
     };
     // Double-buffered key tiles, one barrier per tile: tile t is read from
     // buffer (t - t0) & 1 while tile t+1 is stored into the other buffer
@@ -422,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             if (t * kScoreTile + col < M) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float x = acc[i] * scale_log2;
+                    const float x = acc[i];
                     const float dd = x - mx[i];
                     const float e = __builtin_amdgcn_exp2f(-fabsf(dd));
                     const bool up = dd > 0.0f;
@@ -481,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             for (int g = 0; g < RPW; ++g) pr[g] = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(acc[i] * scale_log2 - mx[i]) * coef[i];
+                const float e = __builtin_amdgcn_exp2f(acc[i] - mx[i]) * coef[i];
                 pr[slot_of(i) / CP] += e;
             }
             const int64_t j = t * kScoreTile + col;
@@ -948,18 +999,18 @@ hipError_t launch_checked(F&& f) {
 }  // namespace
 
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, uint16_t* kbar3, hipStream_t s) {
+                            float* kbar, int8_t* kq, int* kx, hipStream_t s) {
     const int64_t chunks = BH * (N / kKvBlock) * (d / 4);
-    const int threads = 256;
+    const int threads = 256;                    // a multiple of d/4: blocks never straddle
     const int64_t blocks = (chunks + threads - 1) / threads;
     if (blocks == 0) return hipSuccess;
     return launch_checked([&] {
         if (dt == kBF16)
             hipLaunchKernelGGL(mean_keys_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const uint16_t*>(k), kbar, kbar3, chunks, d);
+                               static_cast<const uint16_t*>(k), kbar, kq, kx, chunks, d);
         else
             hipLaunchKernelGGL(mean_keys_kernel<float>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const float*>(k), kbar, kbar3, chunks, d);
+                               static_cast<const float*>(k), kbar, kq, kx, chunks, d);
     });
 }
 
@@ -1016,40 +1067,40 @@ int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C) {
 }
 
 template <int CP, int D>
-static void launch_scores_cpd(const float* cent, const float* w, const uint16_t* kbar3,
-                              int64_t BH, int64_t QB, int64_t M, int C, float2* part,
-                              float* scores, hipStream_t s) {
+static void launch_scores_cpd(const float* cent, const float* w, const int8_t* kq,
+                              const int* kx, int64_t BH, int64_t QB, int64_t M, int C,
+                              float2* part, float* scores, hipStream_t s) {
     constexpr int rows_per_wg = kScoreWaves * (32 / CP);
     int chunk_tiles = 0, nchunks = 0;
     score_chunks(score_groups(BH, QB, C), M, &chunk_tiles, &nchunks);
     const dim3 grid(static_cast<unsigned>((QB + rows_per_wg - 1) / rows_per_wg),
                     static_cast<unsigned>(BH), static_cast<unsigned>(nchunks));
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((scores_kernel<CP, D, false>), grid, dim3(256), 0, s, cent, w, kbar3, QB,
+    hipLaunchKernelGGL((scores_kernel<CP, D, false>), grid, dim3(256), 0, s, cent, w, kq, kx, QB,
                        M, C, chunk_tiles, nchunks, scale_log2, part, scores);
-    hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kbar3, QB,
+    hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kq, kx, QB,
                        M, C, chunk_tiles, nchunks, scale_log2, part, scores);
 }
 
 template <int CP>
-static void launch_scores_cp(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
-                             int64_t QB, int64_t M, int d, int C, float2* part, float* scores,
-                             hipStream_t s) {
+static void launch_scores_cp(const float* cent, const float* w, const int8_t* kq, const int* kx,
+                             int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
+                             float* scores, hipStream_t s) {
     if (d == 128)
-        launch_scores_cpd<CP, 128>(cent, w, kbar3, BH, QB, M, C, part, scores, s);
+        launch_scores_cpd<CP, 128>(cent, w, kq, kx, BH, QB, M, C, part, scores, s);
     else
-        launch_scores_cpd<CP, 64>(cent, w, kbar3, BH, QB, M, C, part, scores, s);
+        launch_scores_cpd<CP, 64>(cent, w, kq, kx, BH, QB, M, C, part, scores, s);
 }
 
-hipError_t launch_scores(const float* cent, const float* w, const uint16_t* kbar3, int64_t BH,
-                         int64_t QB, int64_t M, int d, int C, float2* part, float* scores,
-                         hipStream_t s) {
+hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
+                         int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
+                         float* scores, hipStream_t s) {
     return launch_checked([&] {
-        if (C <= 1) launch_scores_cp<1>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 2) launch_scores_cp<2>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 4) launch_scores_cp<4>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 8) launch_scores_cp<8>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
-        else launch_scores_cp<16>(cent, w, kbar3, BH, QB, M, d, C, part, scores, s);
+        if (C <= 1) launch_scores_cp<1>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 2) launch_scores_cp<2>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 4) launch_scores_cp<4>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
+        else if (C <= 8) launch_scores_cp<8>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
+        else launch_scores_cp<16>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
     });
 }
 
