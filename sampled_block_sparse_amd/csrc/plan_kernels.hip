@@ -411,13 +411,17 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                 *reinterpret_cast<u32x4*>(&ks[buf][key * KROW + c16 * 16]) = pre[i];
             }
         }
-        if (tid < kScoreTile) colf[buf][tid] = __int_as_float((pre_x + 127) << 23);
+        // ldexpf, not an exponent-field write: a mean key below 2^-126 has an
+        // exponent the fp32 normal range does not hold.
+        if (tid < kScoreTile) colf[buf][tid] = ldexpf(1.0f, pre_x);
     };
-    // Scaled logits of the tile: the six digit products of weight >= 2^16
-    // (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2) on the int8 MFMA, combined in
-    // fp32 as 2^16 P22 + 2^8 P21 + P20, times the row and column factors.
-    // The dropped products are below 2^-21 of the dot product's scale.
-    auto tile_logits = [&](int buf) __attribute__((always_inline)) {
+    // Logits of the tile, up to the key's factor: the six digit products of
+    // weight >= 2^16 (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2) on the int8
+    // MFMA, combined as 2^16 P22 + (2^8 P21 + P20) (the bracket is exact in
+    // int32: |P21| <= 2^21 and |P20| < 2^23) and times the row factor. The
+    // logit of row i is tr[i] * cf with cf = 2^(key exponent) of this lane's
+    // key. The dropped products are below 2^-21 of the dot product's scale.
+    auto tile_logits = [&](int buf, float& cf) __attribute__((always_inline)) {
         typedef int intx16 __attribute__((ext_vector_type(16)));
         intx16 p22 = {}, p21 = {}, p20 = {};
         const int8_t* kr = &ks[buf][col * KROW + half * 16];
@@ -433,14 +437,13 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b1, p20, 0, 0, 0);
             p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[st], b2, p20, 0, 0, 0);
         }
-        const float cf = colf[buf][col];
+        cf = colf[buf][col];
         const floatx16 rowf = *reinterpret_cast<const floatx16*>(&rowf_s[wave][half][0]);
         floatx16 x;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float t = fmaf(static_cast<float>(p22[i]), 65536.0f,
-                                 fmaf(static_cast<float>(p21[i]), 256.0f, static_cast<float>(p20[i])));
-            x[i] = (t * rowf[i]) * cf;
+            const int lo = (p21[i] << 8) + p20[i];
+            x[i] = fmaf(static_cast<float>(p22[i]), 65536.0f, static_cast<float>(lo)) * rowf[i];
         }
         return x;
     };
@@ -454,65 +457,84 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         __syncthreads();
         for (int64_t t = t0; t < t1; ++t) {
             const int buf = static_cast<int>((t - t0) & 1);
-            const floatx16 acc = tile_logits(buf);
+            float cf;
+            const floatx16 tr = tile_logits(buf, cf);
             store_tile(buf ^ 1);
             fetch_tile((t + 2 < t1) ? t + 2 : t1 - 1);
-            body(t, acc);
+            body(t, tr, cf);
             __syncthreads();
         }
     };
+    // A lane's key lies past M only in the last tile of the row.
+    const bool ragged = (M % kScoreTile) != 0;
 
     if constexpr (!PASS2) {
-        // Running max and sum per centroid row held by this lane; one
-        // exponential per logit: exp2(-|x - max|) either scales the old sum
-        // (new max) or is the new term.
-        float mx[16], zs[16];
+        // Per centroid row: a reference R (the row's largest logit seen at
+        // the last re-basing, the same in all 32 lanes of the half holding
+        // the row) and the sum of exp2(x - R - kSlack) over this lane's
+        // keys. Kept as nref = -(R + kSlack). A tile whose logits all stay
+        // within R + kSlack costs one FMA, one exponential and one add per
+        // logit; otherwise (and on the first and the ragged tile) the rows
+        // are re-based on their new maxima, a wave-uniform branch.
+        constexpr float kSlack = 16.0f;
+        float nref[16], zs[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { mx[i] = -INFINITY; zs[i] = 0.0f; }
-        for_tiles([&](int64_t t, floatx16 acc) __attribute__((always_inline)) {
-            if (t * kScoreTile + col < M) {
+        for (int i = 0; i < 16; ++i) { nref[i] = INFINITY; zs[i] = 0.0f; }
+        for_tiles([&](int64_t t, floatx16 tr, float cf) __attribute__((always_inline)) {
+            floatx16 dv;
+            float dmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                dv[i] = fmaf(tr[i], cf, nref[i]);
+                dmax = fmaxf(dmax, dv[i]);
+            }
+            const bool last_ragged = ragged && (t + 1) * kScoreTile > M;
+            if (!last_ragged && __builtin_amdgcn_ballot_w64(dmax > 0.0f) == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zs[i] += __builtin_amdgcn_exp2f(dv[i]);
+            } else {
+                const bool ok = t * kScoreTile + col < M;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float x = acc[i];
-                    const float dd = x - mx[i];
-                    const float e = __builtin_amdgcn_exp2f(-fabsf(dd));
-                    const bool up = dd > 0.0f;
-                    zs[i] = up ? fmaf(zs[i], e, 1.0f) : zs[i] + e;
-                    mx[i] = up ? x : mx[i];
+                    const float x = ok ? tr[i] * cf : -INFINITY;
+                    float m = x;
+#pragma unroll
+                    for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+                    const float r_old = -nref[i] - kSlack;
+                    if (m > r_old) {
+                        // r_old = -inf only before the first tile, where zs = 0
+                        zs[i] = (r_old == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(r_old - m);
+                        nref[i] = -(m + kSlack);
+                    }
+                    zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
                 }
             }
         });
-        // Merge the 32 columns of each half (xor over lane bits 0..4).
+        // The reference is uniform over each half: the sums add across its
+        // 32 lanes (xor over lane bits 0..4). Chunk statistic of a row:
+        // (R + kSlack, sum), i.e. the chunk's sum of 2^x is sum * 2^(R + kSlack).
 #pragma unroll
         for (int off = 1; off < 32; off <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float m2 = __shfl_xor(mx[i], off);
-                const float z2 = __shfl_xor(zs[i], off);
-                const float mn = fmaxf(mx[i], m2);
-                const float e1 =
-                    (mx[i] == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(mx[i] - mn);
-                const float e2 = (m2 == -INFINITY) ? 0.0f : z2 * __builtin_amdgcn_exp2f(m2 - mn);
-                zs[i] = e1 + e2;
-                mx[i] = mn;
-            }
+            for (int i = 0; i < 16; ++i) zs[i] += __shfl_xor(zs[i], off);
         }
         if (col == 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int slot = slot_of(i);
-                if (slot_valid(slot)) part[part_index(slot) + chunk] = make_float2(mx[i], zs[i]);
+                if (slot_valid(slot)) part[part_index(slot) + chunk] = make_float2(-nref[i], zs[i]);
             }
         }
     } else {
-        // Max and sum of each centroid over all chunks, in chunk order, and
-        // the coefficient w_m / Z_m of every row this lane holds.
-        float mx[16], coef[16];
+        // Reference and sum of each centroid over all chunks, in chunk
+        // order, folded with the centroid's weight into one exponent bias:
+        // w_m * 2^(x - R) / Z = 2^(x + log2(w_m / Z) - R); -inf for unused
+        // slots (weight 0).
+        float bias[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int slot = slot_of(i);
-            mx[i] = 0.0f;
-            coef[i] = 0.0f;
+            bias[i] = -INFINITY;
             if (slot_valid(slot)) {
                 const float2* pp = part + part_index(slot);
                 float m = -INFINITY;
@@ -522,19 +544,17 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                     const float2 q = pp[c];
                     if (q.x != -INFINITY) z += q.y * __builtin_amdgcn_exp2f(q.x - m);
                 }
-                mx[i] = m;
-                coef[i] = w[(bh * QB + r0 + slot / CP) * C + slot % CP] / z;
+                const float wm = w[(bh * QB + r0 + slot / CP) * C + slot % CP];
+                if (wm > 0.0f) bias[i] = log2f(wm / z) - m;
             }
         }
-        for_tiles([&](int64_t t, floatx16 acc) __attribute__((always_inline)) {
+        for_tiles([&](int64_t t, floatx16 tr, float cf) __attribute__((always_inline)) {
             float pr[RPW];
 #pragma unroll
             for (int g = 0; g < RPW; ++g) pr[g] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(acc[i] - mx[i]) * coef[i];
-                pr[slot_of(i) / CP] += e;
-            }
+            for (int i = 0; i < 16; ++i)
+                pr[slot_of(i) / CP] += __builtin_amdgcn_exp2f(fmaf(tr[i], cf, bias[i]));
             const int64_t j = t * kScoreTile + col;
             if (CP >= 8) {
                 // A query block's clusters span both halves: add the partner's.

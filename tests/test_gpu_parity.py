@@ -161,6 +161,35 @@ def test_cluster_and_iteration_variants(C, T):
     assert score_error(s[good], ref_s.reshape(-1, M)[good]).max() <= SCORE_REL
 
 
+def test_score_magnitude_spread():
+    """Mean keys whose exponents span 2^-133 (bf16 subnormal) to 2^20, with
+    small queries so the logits stay moderate: each key block and each
+    centroid carries its own block floating point exponent in the score
+    contraction, which must hold the fp64 definition's scores to 1e-4."""
+    B, H, N, d = 1, 2, 1024, 128
+    q, k, _ = synth.iid_qkv(B, H, N, d, 21)
+    rng = np.random.default_rng(22)
+    M = N // 4
+    u = np.where(rng.random((B, H, M)) < 0.3, rng.integers(-133, -100, (B, H, M)),
+                 rng.integers(-12, 21, (B, H, M)))
+    k = k * np.repeat(np.exp2(u.astype(np.float64)), 4, axis=2)[..., None]
+    q = q * 2.0 ** -16
+    qt = torch.from_numpy(q).to(torch.bfloat16)
+    kt = torch.from_numpy(k).to(torch.bfloat16)
+    Q, K = to64(qt), to64(kt)
+    plan = absa.absa_plan_create(qt.to(DEV), kt.to(DEV), 26, 3, keep_intermediates=True)
+    s = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M)
+    QB = (N + 127) // 128
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8).reshape(-1, 8)
+    ref_s, _, ref_w = oracle.ibcs_scores(Q, K)
+    bad = np.nonzero((w != ref_w.reshape(-1, 8).astype(np.float32)).any(axis=1))[0]
+    assert flips_explained(Q, bad, N, 8, 4)
+    good = np.setdiff1d(np.arange(B * H * QB), bad)
+    err = score_error(s[good], ref_s.reshape(-1, M)[good])
+    print(f"score error max {err.max():.3e}")
+    assert err.max() <= SCORE_REL
+
+
 def test_minimal_shape():
     q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=4, d=64, seed=3))
     plan = absa.absa_plan_create(q, k, 1, 5)
