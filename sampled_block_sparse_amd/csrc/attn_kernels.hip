@@ -142,11 +142,14 @@ template <int V> using IntC = std::integral_constant<int, V>;
 // at lds_dst + 16 l (global_load_lds_dwordx4, LDS base in M0). Written as
 // inline asm so that the compiler does not order every later LDS read of
 // the workgroup behind it; the loads complete under the kernel's own
-// s_waitcnt vmcnt(0) before the barrier that publishes them. The s_nop is
-// the wait state between the M0 write and its use by the load.
+// s_waitcnt vmcnt(0) before the barrier that publishes them. The s_nop
+// gives the 5 wait states the load needs after a VALU write of its base
+// SGPRs (the compiler may restore spilled SGPRs with v_readlane right
+// before the asm, and does not check hazards inside it); it also covers
+// the one after the M0 write.
 __device__ __forceinline__ void load_to_lds(const char* base, uint32_t off, uint16_t* lds_dst) {
     const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
                  : "memory");
 }
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

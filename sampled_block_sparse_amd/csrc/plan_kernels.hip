@@ -286,6 +286,28 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // slots) for i < 16; operand layout (int8, K = 32): lane l holds row l%32
 // of A and column l%32 of B at k = (l/32)*16 .. +16.
 // ---------------------------------------------------------------------------
+// Loads straight from global memory into LDS: lane l's 16 (or 4) bytes from
+// base + off land at lds_dst + 16 l (or 4 l); base is wave-uniform, lds_dst
+// too (it goes to M0). Written as inline asm so that the compiler does not
+// order every later LDS read of the workgroup behind them; lds_load_wait()
+// (vmcnt(0)) completes them, and a barrier after it publishes them. The
+// s_nop gives the 5 wait states the load needs after a VALU write of its
+// base SGPRs (the compiler may restore spilled SGPRs with v_readlane right
+// before the asm, and does not check hazards inside it); it also covers
+// the one after the M0 write.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, void* lds_dst) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds_dst));
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* base, uint32_t off, void* lds_dst) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds_dst));
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -311,18 +333,17 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     constexpr int RPW = 32 / CP;                    // query blocks per wave
     constexpr int NSTEP = D / 32;                   // MFMA k-steps (32 channels each)
     constexpr int KROW = 3 * D + 16;                // LDS key row (bytes), padded
-    constexpr int CHUNKS = kScoreTile * 3 * D / 16; // 16-byte pieces per tile
-    constexpr int CPT = (CHUNKS + 255) / 256;       // per thread (last pass partial
-                                                    // when CHUNKS % 256 != 0; whole waves)
-    static_assert(CHUNKS % 64 == 0, "tile pieces must split over whole waves");
-    __shared__ __align__(16) int8_t ks[2][kScoreTile * KROW];
-    __shared__ float colf[2][kScoreTile];           // 2^(key exponent) of the tile's keys
+    constexpr int TK = 2 * kScoreTile;              // keys per LDS tile (two 32-key subtiles)
+    constexpr int SROW = KROW / 16;                 // 16-byte slots per LDS key row
+    constexpr int DSLOTS = 3 * D / 16;              // of which hold digits (the last is padding)
+    constexpr int SLOTS = TK * SROW;                // slots per LDS tile: a multiple of 64
+    __shared__ __align__(16) int8_t ks[2][TK * KROW];
+    __shared__ int kxs[2][TK];                      // exponents of the tile's mean keys
     __shared__ int slot_exp[kScoreWaves][32];       // centroid exponents, per wave
-    __shared__ __align__(16) float rowf_s[kScoreWaves][2][16];  // row factors, per half
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
     const int64_t bh = blockIdx.y;
@@ -349,7 +370,11 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             for (int e = 0; e < 16; ++e)
                 amax = fmaxf(amax, slot_ok ? fabsf(src[st * 32 + half * 16 + e]) : 0.0f);
         }
+        // one exponent for the slot pair (s, s^4): the two accumulator rows a
+        // lane holds for element k lie in the two halves of the block, so
+        // each row factor is then the same for the whole wave
         amax = fmaxf(amax, __shfl_xor(amax, 32));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
         const int ex = bfp_exponent(amax);
         if (half == 0) slot_exp[wave][col] = ex;
 #pragma unroll
@@ -376,118 +401,191 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         return ((bh * QB + r0 + slot / CP) * C + slot % CP) * nchunks;
     };
     // Per-row factor: the log2-domain scale times 2^(e_slot - 28) (the digit
-    // sums carry 2^(44 - e_c - e_k), and the combination below 2^-16).
-    // Kept in LDS (read once per tile) rather than in 16 registers.
-    if (col < 16) rowf_s[wave][half][col] = ldexpf(scale_log2, slot_exp[wave][slot_of(col)] - 28);
-    __syncthreads();
+    // sums carry 2^(44 - e_c - e_k), and the combination below 2^-16); the
+    // same in both halves (slot pairs share the exponent), so it is held in
+    // scalar registers.
+    floatx16 rowf;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        rowf[k] = __int_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_int(ldexpf(scale_log2, slot_exp[wave][(k >> 2) * 8 + (k & 3)] - 28))));
 
     const int8_t* kb = kq + bh * M * 3 * D;
     const int* kxb = kx + bh * M;
-    // Native vectors (not uint4 structs): their copies stay in registers.
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 pre[CPT];
-    int pre_x = 0;
-    // Tile loads are unconditional: a key index past M is clamped to M-1 and
-    // its logits are never used, so the loop carries no divergent load.
-    auto fetch_tile = [&](int64_t t) __attribute__((always_inline)) {
-        const int64_t j0 = t * kScoreTile;
+    const int64_t nsub = t1 - t0;                   // 32-key subtiles of this chunk
+    const int64_t nlt = (nsub + 1) / 2;             // 64-key LDS tiles
+    if (nsub <= 0) return;                          // (no empty chunk is launched)
+    // LDS tile u holds keys (t0 + 2u) * 32 .. +64, each as a padded row of
+    // its three digit planes, loaded straight into LDS: the waves' 64-lane
+    // loads fill consecutive 1 KB runs of slots; a slot's key and column
+    // follow from its position, padding slots load a digit slot of the same
+    // key, and keys past M repeat key M-1 (their logits are never used).
+    // 32-bit index arithmetic (M < 2^19), recomputed per tile: the opaque
+    // copy of the lane index keeps the compiler from hoisting the per-lane
+    // offsets of every load out of the loop (they would not fit in registers).
+    const int M32 = static_cast<int>(M);
+    auto dma_tile = [&](int buf, int64_t u) __attribute__((always_inline)) {
+        const int j0 = static_cast<int>((t0 + 2 * u) * kScoreTile);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int e = tid + 256 * i;
-            if (CHUNKS % 256 == 0 || e < CHUNKS) {
-                const int key = e / (3 * D / 16), c16 = e - key * (3 * D / 16);
-                const int64_t j = (j0 + key < M) ? j0 + key : M - 1;
-                pre[i] = *reinterpret_cast<const u32x4*>(kb + j * 3 * D + c16 * 16);
+        for (int i = 0; i < (SLOTS + 255) / 256; ++i) {
+            const int sw = i * 256 + wave * 64;     // wave-uniform
+            if (sw < SLOTS) {
+                const int sl = sw + ln;
+                const int key = sl / SROW, c = sl - key * SROW;
+                const int j = min(j0 + key, M32 - 1);
+                const uint32_t off = static_cast<uint32_t>(j * (3 * D) + (c < DSLOTS ? c : 0) * 16);
+                lds_load16(kb, off, &ks[buf][sw * 16]);
             }
         }
-        if (tid < kScoreTile) pre_x = kxb[(j0 + tid < M) ? j0 + tid : M - 1];
-    };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int e = tid + 256 * i;
-            if (CHUNKS % 256 == 0 || e < CHUNKS) {
-                const int key = e / (3 * D / 16), c16 = e - key * (3 * D / 16);
-                *reinterpret_cast<u32x4*>(&ks[buf][key * KROW + c16 * 16]) = pre[i];
-            }
+        if (wave == 0) {
+            const int j = min(j0 + ln, M32 - 1);
+            lds_load4(kxb, static_cast<uint32_t>(j * 4), &kxs[buf][0]);
         }
-        // ldexpf, not an exponent-field write: a mean key below 2^-126 has an
-        // exponent the fp32 normal range does not hold.
-        if (tid < kScoreTile) colf[buf][tid] = ldexpf(1.0f, pre_x);
     };
-    // Logits of the tile, up to the key's factor: the six digit products of
-    // weight >= 2^16 (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2) on the int8
-    // MFMA, combined as 2^16 P22 + (2^8 P21 + P20) (the bracket is exact in
-    // int32: |P21| <= 2^21 and |P20| < 2^23) and times the row factor. The
-    // logit of row i is tr[i] * cf with cf = 2^(key exponent) of this lane's
-    // key. The dropped products are below 2^-21 of the dot product's scale.
-    auto tile_logits = [&](int buf, float& cf) __attribute__((always_inline)) {
-        typedef int intx16 __attribute__((ext_vector_type(16)));
-        intx16 p22 = {}, p21 = {}, p20 = {};
-        const int8_t* kr = &ks[buf][col * KROW + half * 16];
+    typedef int intx16 __attribute__((ext_vector_type(16)));
+    // Logit of accumulator row k, up to the key's factor: the six digit
+    // products of weight >= 2^16 (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2)
+    // combined as 2^16 P22 + (2^8 P21 + P20) (the bracket is exact in int32:
+    // |P21| <= 2^21, |P20| < 2^23) times the row factor. The logit is this
+    // times 2^(key exponent); the dropped products are below 2^-21 of the
+    // dot product's scale.
+    auto combine = [&](const intx16& i22, const intx16& i21, const intx16& i20,
+                       const floatx16& rowf, int k) __attribute__((always_inline)) {
+        const int lo = (i21[k] << 8) + i20[k];
+        return fmaf(static_cast<float>(i22[k]), 65536.0f, static_cast<float>(lo)) * rowf[k];
+    };
+    auto key_factor = [&](int buf, int key) __attribute__((always_inline)) {
+        return ldexpf(1.0f, kxs[buf][key]);
+    };
+    // One subtile's digit products (subtile sb of buffer buf) into o22/o21/o20,
+    // with item(k) (the VALU work of row k of the previous subtile) spread
+    // between the MFMAs; the B operands are read one k-step ahead.
+    constexpr int NM = 6 * NSTEP;
+    auto phase = [&](int buf, int sb, intx16& o22, intx16& o21, intx16& o20,
+                     auto&& item) __attribute__((always_inline)) {
+        const int8_t* kr = &ks[buf][(sb * kScoreTile + col) * KROW + half * 16];
+        auto ld = [&](int off) { return *reinterpret_cast<const intx4*>(kr + off); };
+        intx4 b2 = ld(0), b1 = ld(D), b0 = ld(2 * D);
+        o22 = intx16{};
+        o21 = intx16{};
+        o20 = intx16{};
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-            const intx4 b2 = *reinterpret_cast<const intx4*>(kr + st * 32);
-            const intx4 b1 = *reinterpret_cast<const intx4*>(kr + D + st * 32);
-            const intx4 b0 = *reinterpret_cast<const intx4*>(kr + 2 * D + st * 32);
-            p22 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b2, p22, 0, 0, 0);
-            p21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b1, p21, 0, 0, 0);
-            p21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b2, p21, 0, 0, 0);
-            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b0, p20, 0, 0, 0);
-            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b1, p20, 0, 0, 0);
-            p20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[st], b2, p20, 0, 0, 0);
-        }
-        cf = colf[buf][col];
-        const floatx16 rowf = *reinterpret_cast<const floatx16*>(&rowf_s[wave][half][0]);
-        floatx16 x;
+            intx4 n2 = b2, n1 = b1, n0 = b0;
+            if (st + 1 < NSTEP) {
+                n2 = ld((st + 1) * 32);
+                n1 = ld(D + (st + 1) * 32);
+                n0 = ld(2 * D + (st + 1) * 32);
+            }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int lo = (p21[i] << 8) + p20[i];
-            x[i] = fmaf(static_cast<float>(p22[i]), 65536.0f, static_cast<float>(lo)) * rowf[i];
+            for (int m = 0; m < 6; ++m) {
+                if (m == 0) o20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b0, o20, 0, 0, 0);
+                if (m == 1) o21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b1, o21, 0, 0, 0);
+                if (m == 2) o22 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2[st], b2, o22, 0, 0, 0);
+                if (m == 3) o20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b1, o20, 0, 0, 0);
+                if (m == 4) o21 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[st], b2, o21, 0, 0, 0);
+                if (m == 5) o20 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[st], b2, o20, 0, 0, 0);
+                const int mi = st * 6 + m;
+#pragma unroll
+                for (int k = mi * 16 / NM; k < (mi + 1) * 16 / NM; ++k) item(k);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            b2 = n2;
+            b1 = n1;
+            b0 = n0;
         }
-        return x;
     };
-    // Double-buffered key tiles, one barrier per tile: tile t is read from
-    // buffer (t - t0) & 1 while tile t+1 is stored into the other buffer
-    // (last read before the previous barrier) and tile t+2 is loaded.
-    auto for_tiles = [&](auto&& body) __attribute__((always_inline)) {
-        fetch_tile(t0);
-        store_tile(0);
-        fetch_tile((t0 + 1 < t1) ? t0 + 1 : t0);
+    // Pipeline over LDS tiles, one barrier per tile: iteration u runs the
+    // products of subtile 2u+1 (into set B) beside the VALU work of subtile
+    // 2u (set A), then, after the barrier that publishes tile u+1 (loaded
+    // from the start of iteration u into the other buffer, which iteration
+    // u-1 finished reading before its barrier), the products of subtile
+    // 2u+2 (set A) beside the VALU work of subtile 2u+1 (set B). item(...)
+    // does the VALU work of one row of a subtile given its accumulators and
+    // key factor, post(g, ...) finishes subtile g after its phase, and
+    // first(...) runs on subtile 0 alone before the loop.
+    intx16 xa22, xa21, xa20, xb22, xb21, xb20;
+    auto pipeline = [&](auto&& item, auto&& pre, auto&& post, auto&& first) __attribute__((always_inline)) {
+        auto none = [](int) {};
+        dma_tile(0, 0);
+        lds_load_wait();
         __syncthreads();
-        for (int64_t t = t0; t < t1; ++t) {
-            const int buf = static_cast<int>((t - t0) & 1);
-            float cf;
-            const floatx16 tr = tile_logits(buf, cf);
-            store_tile(buf ^ 1);
-            fetch_tile((t + 2 < t1) ? t + 2 : t1 - 1);
-            body(t, tr, cf);
+        phase(0, 0, xa22, xa21, xa20, none);
+        first(xa22, xa21, xa20, key_factor(0, col));
+        for (int64_t u = 0; u < nlt; ++u) {
+            const int buf = static_cast<int>(u & 1);
+            if (u + 1 < nlt) dma_tile(buf ^ 1, u + 1);
+            {
+                const float cf = key_factor(buf, col);
+                pre();
+                phase(buf, 1, xb22, xb21, xb20,
+                      [&](int k) { item(xa22, xa21, xa20, rowf, cf, k); });
+                post(2 * u, xa22, xa21, xa20, cf);
+            }
+            // key factor of subtile 2u+1, read before the barrier after which
+            // the next iteration's loads may overwrite this buffer
+            const float cf1 = key_factor(buf, kScoreTile + col);
+            lds_load_wait();
             __syncthreads();
+            if (2 * u + 1 < nsub) {
+                pre();
+                phase(buf ^ 1, 0, xa22, xa21, xa20,
+                      [&](int k) { item(xb22, xb21, xb20, rowf, cf1, k); });
+                post(2 * u + 1, xb22, xb21, xb20, cf1);
+            }
         }
     };
-    // A lane's key lies past M only in the last tile of the row.
+    // A lane's key lies past M only in the last subtile of the row.
     const bool ragged = (M % kScoreTile) != 0;
 
     if constexpr (!PASS2) {
         // Per centroid row: a reference R (the row's largest logit seen at
         // the last re-basing, the same in all 32 lanes of the half holding
         // the row) and the sum of exp2(x - R - kSlack) over this lane's
-        // keys. Kept as nref = -(R + kSlack). A tile whose logits all stay
+        // keys. Kept as nref = -(R + kSlack). A subtile whose logits all stay
         // within R + kSlack costs one FMA, one exponential and one add per
-        // logit; otherwise (and on the first and the ragged tile) the rows
-        // are re-based on their new maxima, a wave-uniform branch.
+        // logit (computed beside the next subtile's products); otherwise
+        // (and on the first and the ragged subtile) the rows are re-based on
+        // their new maxima, a wave-uniform branch.
         constexpr float kSlack = 16.0f;
-        float nref[16], zs[16];
+        float nref[16], zs[16], dv[16];
+        float dmax = -INFINITY;
+        // Re-basing of row i on the logits x of a subtile (x = -inf past M):
+        // R = max(R, the half's largest x), the sum rescaled to the new R.
+        auto rebase = [&](int i, float x) __attribute__((always_inline)) {
+            float m = x;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+            const float r_old = -nref[i] - kSlack;
+            if (m > r_old) {
+                // r_old = -inf only on subtile 0, where zs = 0
+                zs[i] = (r_old == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(r_old - m);
+                nref[i] = -(m + kSlack);
+            }
+            zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
+        };
 #pragma unroll
         for (int i = 0; i < 16; ++i) { nref[i] = INFINITY; zs[i] = 0.0f; }
-        for_tiles([&](int64_t t, floatx16 tr, float cf) __attribute__((always_inline)) {
-            floatx16 dv;
-            float dmax = -INFINITY;
+        // Subtile 0 sets the references from its exact logits.
+        auto first = [&](const intx16& i22, const intx16& i21, const intx16& i20,
+                         float cf) __attribute__((always_inline)) {
+            const bool ok = t0 * kScoreTile + col < M;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                dv[i] = fmaf(tr[i], cf, nref[i]);
-                dmax = fmaxf(dmax, dv[i]);
-            }
+            for (int i = 0; i < 16; ++i) rebase(i, ok ? combine(i22, i21, i20, rowf, i) * cf : -INFINITY);
+        };
+        auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
+                        const floatx16& rf, float cf, int k) __attribute__((always_inline)) {
+            dv[k] = fmaf(combine(i22, i21, i20, rf, k), cf, nref[k]);
+            dmax = fmaxf(dmax, dv[k]);
+        };
+        auto pre = [&]() __attribute__((always_inline)) { dmax = -INFINITY; };
+        // Subtiles g >= 1: the references are finite, so x = dv - nref.
+        auto post = [&](int64_t g, const intx16&, const intx16&, const intx16&,
+                        float) __attribute__((always_inline)) {
+            if (g == 0) return;
+            const int64_t t = t0 + g;
             const bool last_ragged = ragged && (t + 1) * kScoreTile > M;
             if (!last_ragged && __builtin_amdgcn_ballot_w64(dmax > 0.0f) == 0) {
 #pragma unroll
@@ -495,21 +593,10 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             } else {
                 const bool ok = t * kScoreTile + col < M;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float x = ok ? tr[i] * cf : -INFINITY;
-                    float m = x;
-#pragma unroll
-                    for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-                    const float r_old = -nref[i] - kSlack;
-                    if (m > r_old) {
-                        // r_old = -inf only before the first tile, where zs = 0
-                        zs[i] = (r_old == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(r_old - m);
-                        nref[i] = -(m + kSlack);
-                    }
-                    zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
-                }
+                for (int i = 0; i < 16; ++i) rebase(i, ok ? dv[i] - nref[i] : -INFINITY);
             }
-        });
+        };
+        pipeline(item, pre, post, first);
         // The reference is uniform over each half: the sums add across its
         // 32 lanes (xor over lane bits 0..4). Chunk statistic of a row:
         // (R + kSlack, sum), i.e. the chunk's sum of 2^x is sum * 2^(R + kSlack).
@@ -548,33 +635,39 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                 if (wm > 0.0f) bias[i] = log2f(wm / z) - m;
             }
         }
-        for_tiles([&](int64_t t, floatx16 tr, float cf) __attribute__((always_inline)) {
-            float pr[RPW];
+        float pr[RPW];
+        auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
+                        const floatx16& rowf, float cf, int k) __attribute__((always_inline)) {
+            pr[slot_of(k) / CP] +=
+                __builtin_amdgcn_exp2f(fmaf(combine(i22, i21, i20, rowf, k), cf, bias[k]));
+        };
+        auto pre = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int g = 0; g < RPW; ++g) pr[g] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                pr[slot_of(i) / CP] += __builtin_amdgcn_exp2f(fmaf(tr[i], cf, bias[i]));
-            const int64_t j = t * kScoreTile + col;
+        };
+        auto post = [&](int64_t g, const intx16&, const intx16&, const intx16&,
+                        float) __attribute__((always_inline)) {
+            const int64_t j = (t0 + g) * kScoreTile + col;
             if (CP >= 8) {
                 // A query block's clusters span both halves: add the partner's.
 #pragma unroll
-                for (int g = 0; g < RPW; ++g) pr[g] += __shfl_xor(pr[g], 32);
+                for (int q = 0; q < RPW; ++q) pr[q] += __shfl_xor(pr[q], 32);
 #pragma unroll
-                for (int g = 0; g < RPW; ++g) {
-                    const int64_t rr = r0 + g;
-                    if ((g & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[g];
+                for (int q = 0; q < RPW; ++q) {
+                    const int64_t rr = r0 + q;
+                    if ((q & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[q];
                 }
             } else {
 #pragma unroll
-                for (int g = 0; g < RPW; ++g) {
-                    // rows g whose slots lie in this lane's half
-                    const int half_of_g = ((g * CP) >> 2) & 1;
-                    const int64_t rr = r0 + g;
-                    if (half_of_g == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[g];
+                for (int q = 0; q < RPW; ++q) {
+                    // rows q whose slots lie in this lane's half
+                    const int half_of_q = ((q * CP) >> 2) & 1;
+                    const int64_t rr = r0 + q;
+                    if (half_of_q == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[q];
                 }
             }
-        });
+        };
+        pipeline(item, pre, post, [](const intx16&, const intx16&, const intx16&, float) {});
     }
 }
 
