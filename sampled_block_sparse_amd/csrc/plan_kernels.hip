@@ -286,6 +286,15 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // slots) for i < 16; operand layout (int8, K = 32): lane l holds row l%32
 // of A and column l%32 of B at k = (l/32)*16 .. +16.
 // ---------------------------------------------------------------------------
+// Position of 16-byte slot c of key k in the key's row of a score tile
+// plane: c ^ score_swizzle(k). Over any 8 (or 16) consecutive keys read at
+// the same slot, the addresses fall in distinct 16-byte bank groups of a
+// 128-byte (or 256-byte) LDS row, for rows of 128 bytes (D = 128) and of 64
+// bytes (D = 64).
+template <int D> __device__ __forceinline__ int score_swizzle(int k) {
+    return (D == 128) ? ((k & 7) ^ ((k >> 3) & 1)) : (((k >> 1) & 3) ^ ((k >> 3) & 1));
+}
+
 // Loads straight from global memory into LDS: lane l's 16 (or 4) bytes from
 // base + off land at lds_dst + 16 l (or 4 l); base is wave-uniform, lds_dst
 // too (it goes to M0). Written as inline asm so that the compiler does not
@@ -332,12 +341,12 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                                                         float* __restrict__ scores) {
     constexpr int RPW = 32 / CP;                    // query blocks per wave
     constexpr int NSTEP = D / 32;                   // MFMA k-steps (32 channels each)
-    constexpr int KROW = 3 * D + 16;                // LDS key row (bytes), padded
     constexpr int TK = 2 * kScoreTile;              // keys per LDS tile (two 32-key subtiles)
-    constexpr int SROW = KROW / 16;                 // 16-byte slots per LDS key row
-    constexpr int DSLOTS = 3 * D / 16;              // of which hold digits (the last is padding)
-    constexpr int SLOTS = TK * SROW;                // slots per LDS tile: a multiple of 64
-    __shared__ __align__(16) int8_t ks[2][TK * KROW];
+    constexpr int PL = TK * D;                      // bytes of one digit plane of a tile
+    constexpr int SPR = D / 16;                     // 16-byte slots per key row of a plane
+    constexpr int SLOTS = 3 * TK * SPR;             // slots per LDS tile: a multiple of 256
+    static_assert(SLOTS % 256 == 0, "tile slots must split evenly over the threads");
+    __shared__ __align__(16) int8_t ks[2][3 * PL];
     __shared__ int kxs[2][TK];                      // exponents of the tile's mean keys
     __shared__ int slot_exp[kScoreWaves][32];       // centroid exponents, per wave
 
@@ -415,11 +424,13 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     const int64_t nsub = t1 - t0;                   // 32-key subtiles of this chunk
     const int64_t nlt = (nsub + 1) / 2;             // 64-key LDS tiles
     if (nsub <= 0) return;                          // (no empty chunk is launched)
-    // LDS tile u holds keys (t0 + 2u) * 32 .. +64, each as a padded row of
-    // its three digit planes, loaded straight into LDS: the waves' 64-lane
-    // loads fill consecutive 1 KB runs of slots; a slot's key and column
-    // follow from its position, padding slots load a digit slot of the same
-    // key, and keys past M repeat key M-1 (their logits are never used).
+    // LDS tile u holds keys (t0 + 2u) * 32 .. +64 plane by plane (X2, X1, X0;
+    // a key's row of a plane is D bytes), loaded straight into LDS: the
+    // waves' 64-lane loads fill consecutive 1 KB runs of slots. Slot c of key
+    // k is stored at c ^ score_swizzle(k) within the row, so that the B
+    // operand reads (one slot of 32 consecutive keys) hit distinct banks; a
+    // stored slot's key and logical slot follow from its position. Keys past
+    // M repeat key M-1 (their logits are never used).
     // 32-bit index arithmetic (M < 2^19), recomputed per tile: the opaque
     // copy of the lane index keeps the compiler from hoisting the per-lane
     // offsets of every load out of the loop (they would not fit in registers).
@@ -428,16 +439,16 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         const int j0 = static_cast<int>((t0 + 2 * u) * kScoreTile);
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        const int lk = ln / SPR, cs = ln % SPR;    // key offset and stored slot of the lane
 #pragma unroll
-        for (int i = 0; i < (SLOTS + 255) / 256; ++i) {
-            const int sw = i * 256 + wave * 64;     // wave-uniform
-            if (sw < SLOTS) {
-                const int sl = sw + ln;
-                const int key = sl / SROW, c = sl - key * SROW;
-                const int j = min(j0 + key, M32 - 1);
-                const uint32_t off = static_cast<uint32_t>(j * (3 * D) + (c < DSLOTS ? c : 0) * 16);
-                lds_load16(kb, off, &ks[buf][sw * 16]);
-            }
+        for (int i = 0; i < SLOTS / 256; ++i) {
+            const int sw = i * 256 + wave * 64;     // wave-uniform; a run stays in one plane
+            const int p = sw / (TK * SPR);
+            const int k = (sw / SPR) % TK + lk;
+            const int c = cs ^ score_swizzle<D>(k);
+            const int j = min(j0 + k, M32 - 1);
+            const uint32_t off = static_cast<uint32_t>(j * (3 * D) + p * D + c * 16);
+            lds_load16(kb, off, &ks[buf][sw * 16]);
         }
         if (wave == 0) {
             const int j = min(j0 + ln, M32 - 1);
@@ -465,9 +476,14 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     constexpr int NM = 6 * NSTEP;
     auto phase = [&](int buf, int sb, intx16& o22, intx16& o21, intx16& o20,
                      auto&& item) __attribute__((always_inline)) {
-        const int8_t* kr = &ks[buf][(sb * kScoreTile + col) * KROW + half * 16];
-        auto ld = [&](int off) { return *reinterpret_cast<const intx4*>(kr + off); };
-        intx4 b2 = ld(0), b1 = ld(D), b0 = ld(2 * D);
+        const int key = sb * kScoreTile + col;
+        const int8_t* kr = &ks[buf][key * D];
+        const int sz = score_swizzle<D>(key);
+        // plane p, k-step st: logical slot 2 st + half of the key's row
+        auto ld = [&](int p, int st) {
+            return *reinterpret_cast<const intx4*>(kr + p * PL + 16 * ((2 * st + half) ^ sz));
+        };
+        intx4 b2 = ld(0, 0), b1 = ld(1, 0), b0 = ld(2, 0);
         o22 = intx16{};
         o21 = intx16{};
         o20 = intx16{};
@@ -475,9 +491,9 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         for (int st = 0; st < NSTEP; ++st) {
             intx4 n2 = b2, n1 = b1, n0 = b0;
             if (st + 1 < NSTEP) {
-                n2 = ld((st + 1) * 32);
-                n1 = ld(D + (st + 1) * 32);
-                n0 = ld(2 * D + (st + 1) * 32);
+                n2 = ld(0, st + 1);
+                n1 = ld(1, st + 1);
+                n0 = ld(2, st + 1);
             }
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
@@ -551,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         // their new maxima, a wave-uniform branch.
         constexpr float kSlack = 16.0f;
         float nref[16], zs[16], dv[16];
-        float dmax = -INFINITY;
+        bool over = false;
         // Re-basing of row i on the logits x of a subtile (x = -inf past M):
         // R = max(R, the half's largest x), the sum rescaled to the new R.
         auto rebase = [&](int i, float x) __attribute__((always_inline)) {
@@ -564,7 +580,6 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                 zs[i] = (r_old == -INFINITY) ? 0.0f : zs[i] * __builtin_amdgcn_exp2f(r_old - m);
                 nref[i] = -(m + kSlack);
             }
-            zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
         };
 #pragma unroll
         for (int i = 0; i < 16; ++i) { nref[i] = INFINITY; zs[i] = 0.0f; }
@@ -573,28 +588,40 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                          float cf) __attribute__((always_inline)) {
             const bool ok = t0 * kScoreTile + col < M;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) rebase(i, ok ? combine(i22, i21, i20, rowf, i) * cf : -INFINITY);
+            for (int i = 0; i < 16; ++i) {
+                const float x = ok ? combine(i22, i21, i20, rowf, i) * cf : -INFINITY;
+                rebase(i, x);
+                zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
+            }
         };
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
                         const floatx16& rf, float cf, int k) __attribute__((always_inline)) {
             dv[k] = fmaf(combine(i22, i21, i20, rf, k), cf, nref[k]);
-            dmax = fmaxf(dmax, dv[k]);
+            over = over || dv[k] > 0.0f;
+            // pinned here, between the MFMAs: the compiler would otherwise
+            // sink the whole computation past them, next to its use
+            asm volatile("" : "+v"(dv[k]));
         };
-        auto pre = [&]() __attribute__((always_inline)) { dmax = -INFINITY; };
-        // Subtiles g >= 1: the references are finite, so x = dv - nref.
+        auto pre = [&]() __attribute__((always_inline)) { over = false; };
+        // Subtiles g >= 1 (the references are finite, so x = dv - nref): a
+        // rare re-basing rewrites dv in place, then every subtile adds its
+        // exponentials.
         auto post = [&](int64_t g, const intx16&, const intx16&, const intx16&,
                         float) __attribute__((always_inline)) {
             if (g == 0) return;
             const int64_t t = t0 + g;
             const bool last_ragged = ragged && (t + 1) * kScoreTile > M;
-            if (!last_ragged && __builtin_amdgcn_ballot_w64(dmax > 0.0f) == 0) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) zs[i] += __builtin_amdgcn_exp2f(dv[i]);
-            } else {
+            if (last_ragged || __builtin_amdgcn_ballot_w64(over) != 0) {
                 const bool ok = t * kScoreTile + col < M;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) rebase(i, ok ? dv[i] - nref[i] : -INFINITY);
+                for (int i = 0; i < 16; ++i) {
+                    const float x = ok ? dv[i] - nref[i] : -INFINITY;
+                    rebase(i, x);
+                    dv[i] = x + nref[i];
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zs[i] += __builtin_amdgcn_exp2f(dv[i]);
         };
         pipeline(item, pre, post, first);
         // The reference is uniform over each half: the sums add across its
