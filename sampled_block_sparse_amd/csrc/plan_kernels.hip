@@ -789,6 +789,20 @@ __device__ __forceinline__ double fixed_point(float s) {
     return floor(static_cast<double>(s) * 0x1.0p52);
 }
 
+// Sum of fixed-point scores kept in two parts: scores >= 2^-29 have an ulp of
+// at least 2^-52, so floor(s * 2^52) = s * 2^52 exactly and they are summed as
+// s (every such sum is a multiple of 2^-52 below 2: exact); smaller scores are
+// summed as fixed_point(s). value() = 2^52 * big + small, both exact integers
+// below 2^53, so the sum is the same exact integer in any order.
+struct FixedSum {
+    double big = 0.0, small = 0.0;
+    __device__ __forceinline__ void add(float s) {
+        if (s >= 0x1.0p-29f) big += static_cast<double>(s);
+        else small += fixed_point(s);
+    }
+    __device__ __forceinline__ double value() const { return big * 0x1.0p52 + small; }
+};
+
 // p of block j given the row's outcome; capped blocks have p = 1.
 __device__ __forceinline__ double sip_p(bool capped, const SipRow& ri, float s) {
     if (capped || ri.mode == 0) return 1.0;
@@ -804,12 +818,9 @@ __device__ __forceinline__ double cap_threshold(double c) {
     double t = ceil(1.0 / c);
     if (!(t < 0x1.0p53)) t = 0x1.0p53;
     if (t < 1.0) t = 1.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (t > 1.0 && c * (t - 1.0) >= 1.0) t -= 1.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (t < 0x1.0p53 && c * t < 1.0) t += 1.0;
+    // at most a few steps each (c is uniform, so are the exits)
+    for (int i = 0; i < 4 && t > 1.0 && c * (t - 1.0) >= 1.0; ++i) t -= 1.0;
+    for (int i = 0; i < 4 && t < 0x1.0p53 && c * t < 1.0; ++i) t += 1.0;
     return t;
 }
 
@@ -875,13 +886,13 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         else return load_pair(tid + k * kSipPairsPerPass);
     };
 
-    double sum = 0.0;
+    FixedSum sum;
     int bad = 0;
     float vmax = -1.0f;            // largest score of this thread not yet capped
     auto add_score = [&](float v, int j) {
         if (j >= M32) return;
         if (!(v >= 0.0f && v <= 1.0f)) bad = 1;
-        else sum += fixed_point(v);
+        else sum.add(v);
         vmax = fmaxf(vmax, v);
     };
     if constexpr (MAXP > 0) {
@@ -903,7 +914,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
             add_score(v.y, 2 * i + 1);
         }
     }
-    const double total = block_sum(sum, redd);
+    const double total = block_sum(sum.value(), redd);
     const int nbad = block_sum(bad, redi);
     if (nbad != 0 || total >= 0x1.0p53) {
         if (tid == 0) {
@@ -931,14 +942,14 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         const double c = static_cast<double>(left) / S;
         const float thr = fp32_at_least(cap_threshold(c) * 0x1.0p-52);
         int ncap = 0;
-        double scap = 0.0;
+        FixedSum scap;
         auto test = [&](float v) {
-            // opaque copy: keeps fixed_point(v) of every block from being
+            // opaque copy: keeps the conversions of every block from being
             // hoisted out of the rounds loop (64 live doubles otherwise)
             asm volatile("" : "+v"(v));
             if (v >= thr && v < thr_min) {
                 ++ncap;
-                scap += fixed_point(v);
+                scap.add(v);
             }
         };
         if constexpr (MAXP > 0) {
@@ -962,7 +973,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         // integers below 2^53, exact in any order)
         int tcap;
         double tsum;
-        block_sum2(ncap, scap, redi, redd, tcap, tsum);
+        block_sum2(ncap, scap.value(), redi, redd, tcap, tsum);
         if (tcap == 0) { ri.mode = 2; ri.c = c; break; }
         taken += tcap;
         n_active -= tcap;
