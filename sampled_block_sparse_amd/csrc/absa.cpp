@@ -415,7 +415,8 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
         // own buffers (and the intermediates it keeps) from the pool.
         auto temps = [&](auto& a, PlanTemps& t) -> absa_status {
             if (!keep_inter) {
-                ABSA_TRY(a.alloc(&t.kbar, B * H * M * d, "mean keys"));
+                // the fp32 means are only exported; the scores use their digits
+                t.kbar = nullptr;
                 ABSA_TRY(a.alloc(&t.cent, P->rows * C * d, "centroids"));
                 ABSA_TRY(a.alloc(&t.w, P->rows * C, "cluster weights"));
                 ABSA_TRY(a.alloc(&t.scores, P->rows * M, "scores"));

@@ -34,7 +34,7 @@ struct PlanStatus {
     int32_t pad;
 };
 
-// kbar: fp32 means [BH, M, d]; kq: their block floating point int8 digits
+// kbar: fp32 means [BH, M, d], or null to skip them; kq: their block floating point int8 digits
 // [BH, M, 3, d] (planes X2, X1, X0) and kx: the exponent of each mean [BH, M],
 // the score kernel's operand.
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,

@@ -57,7 +57,9 @@ __device__ __forceinline__ void bfp_digits(float x, int e, int8_t& d2, int8_t& d
 // consecutive lanes; the fp32 sum of four bf16 values is exact unless their
 // exponents differ by more than 15. Also writes each mean's block floating
 // point form, the operand of the score kernel's matrix products: digit
-// planes kq[bh, j, plane, :] (plane 0 = X2) and the exponent kx[bh, j].
+// planes kq[bh, j, plane, :] (plane 0 = X2) and the exponent kx[bh, j]. The
+// fp32 means are written only when kbar is not null (they are exported, not
+// used by the scores).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
     float amax = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
     for (int off = 1; off < per_row; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if (!ok) return;
-    *reinterpret_cast<float4*>(kbar + blk * d + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if (kbar) *reinterpret_cast<float4*>(kbar + blk * d + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     const int ex = bfp_exponent(amax);
     int8_t pl[3][4];
 #pragma unroll
@@ -274,14 +276,16 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // KV blocks of the head. This is a dense contraction (centroids x mean keys,
 // per head) that must be accurate to 1e-4 relative; it runs on the int8 MFMA
 // (32x32x32) on block floating point forms of both operands (three int8
-// digits per value, one exponent per centroid and per mean key), summing
-// the six digit products of weight >= 2^16 in int32 accumulators (exact)
-// and combining them in fp32; the result carries about 2^-21 of the dot
-// product's scale. A wave owns 32 centroid slots (32/CP query blocks of CP
-// slots; slots past C have weight 0) against 32-key tiles staged in LDS.
-// Pass 1 keeps per-lane running (max, sum) of each centroid's exponentials
-// and merges them across lanes; pass 2 recomputes the logits and writes the
-// weighted sum over the block's clusters. MFMA D layout (32x32): lane l
+// digits per value, one exponent per mean key and per pair of centroid
+// slots), summing the six digit products of weight >= 2^16 in int32
+// accumulators (exact) and combining them in fp32; the result carries about
+// 2^-21 of the dot product's scale. A wave owns 32 centroid slots (32/CP
+// query blocks of CP slots; slots past C have weight 0) against 64-key tiles
+// loaded straight into LDS, as two 32-key subtiles whose products overlap
+// the VALU work of the previous subtile. Pass 1 keeps, per centroid row, a
+// reference and the sum of the exponentials relative to it, merged across
+// lanes; pass 2 recomputes the logits and writes the weighted sum over the
+// block's clusters. MFMA D layout (32x32): lane l
 // holds column l%32 (a key) and rows (i/4)*8 + (l/32)*4 + i%4 (centroid
 // slots) for i < 16; operand layout (int8, K = 32): lane l holds row l%32
 // of A and column l%32 of B at k = (l/32)*16 .. +16.
