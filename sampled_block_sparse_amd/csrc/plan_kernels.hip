@@ -1088,6 +1088,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
 // each wave expands 64 of the chunk's words one at a time, lane l handling
 // bit l, so a word's kept blocks are written by consecutive lanes to
 // consecutive positions (v_mbcnt gives each lane its rank in the word).
+// Blocks with p = 1 (capped, or every block in mode 0) and mode 1's uniform
+// p are written at once. The kept blocks of mode 2 that are not capped
+// (about one per word) need their score, p = c * q and an fp64 logarithm:
+// they are queued per wave in LDS and handled 64 at a time, one per lane,
+// so each logarithm instruction serves a full wave instead of one lane.
 __global__ __launch_bounds__(256) void sip_fill_kernel(
     const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
     const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
@@ -1095,6 +1100,8 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     double* __restrict__ p_out) {
     __shared__ int wtot[4];
     __shared__ int word_pos[256];
+    __shared__ int64_t q_at[4][64];                    // queued output positions, per wave
+    __shared__ int q_j[4][64];                         // and their block indices
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int words = static_cast<int>((M + 63) / 64);
@@ -1103,6 +1110,20 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     const SipRow ri = rowinfo[row];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // p and -ln p of a block that is neither capped nor queued
+    const double p_direct = (ri.mode == 1) ? ri.c : 1.0;
+    const float lw_direct = (p_direct == 1.0) ? 0.0f : static_cast<float>(-log(p_direct));
+    int nq = 0;                                        // queue length (wave-uniform)
+    auto flush = [&]() {
+        if (lane < nq) {
+            const int64_t at = q_at[wave][lane];
+            const int j = q_j[wave][lane];
+            const double p = sip_p(false, ri, sg[j]);
+            logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
+            p_out[at] = p;
+        }
+        nq = 0;
+    };
     int64_t pos = rowptr[row];
     for (int base = 0; base < words; base += 256) {
         const int w = base + tid;
@@ -1128,18 +1149,29 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
             const uint64_t kw = km[base + wl];            // wave-uniform
             if (kw == 0) continue;
             const uint64_t cw = cm[base + wl];
+            const uint64_t qw = (ri.mode == 2) ? (kw & ~cw) : 0ull;   // blocks to queue
+            const int nqw = __popcll(qw);
+            if (nq + nqw > 64) flush();
             if ((kw >> lane) & 1ull) {
                 const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(kw >> 32),
                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(kw), 0));
                 const int64_t at = pos + word_pos[wl] + rank;
-                const int64_t j = static_cast<int64_t>(base + wl) * 64 + lane;
-                const bool capped = (cw >> lane) & 1ull;
-                const double p = capped ? 1.0 : sip_p(false, ri, sg[j]);
-                idx[at] = static_cast<int32_t>(j);
-                logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
-                p_out[at] = p;
+                const int j = (base + wl) * 64 + lane;
+                idx[at] = j;
+                if ((qw >> lane) & 1ull) {
+                    const int qr = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(qw >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(qw), 0));
+                    q_at[wave][nq + qr] = at;
+                    q_j[wave][nq + qr] = j;
+                } else {
+                    const bool capped = (cw >> lane) & 1ull;
+                    logw[at] = capped ? 0.0f : lw_direct;
+                    p_out[at] = capped ? 1.0 : p_direct;
+                }
             }
+            nq += nqw;
         }
+        flush();
         pos += tot;
         __syncthreads();
     }
