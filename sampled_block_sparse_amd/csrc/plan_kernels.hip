@@ -451,7 +451,8 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             const int k = (sw / SPR) % TK + lk;
             const int c = cs ^ score_swizzle<D>(k);
             const int j = min(j0 + k, M32 - 1);
-            const uint32_t off = static_cast<uint32_t>(j * (3 * D) + p * D + c * 16);
+            // j < 2^19: a full-rate 24-bit multiply
+            const uint32_t off = __umul24(static_cast<uint32_t>(j), 3 * D) + p * D + c * 16;
             lds_load16(kb, off, &ks[buf][sw * 16]);
         }
         if (wave == 0) {
@@ -840,9 +841,9 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // SIP probabilities and draws [hamidun, SIP paragraph; edumints, SIP item]:
 // capped water-filling in exact fixed point (q_j = floor(s_j 2^52), exact
 // sums, IEEE double division and product), then one Poisson draw per block.
-// One workgroup of 512 threads per plan row. Thread t owns the block pairs
-// (2i, 2i+1) with i = t + 512 k; with MAXP > 0 it keeps their scores in
-// registers (rows of up to 1024 * MAXP blocks), otherwise every pass
+// One workgroup of NT threads per plan row. Thread t owns the block pairs
+// (2i, 2i+1) with i = t + NT k; with MAXP > 0 it keeps their scores in
+// registers (rows of up to 2 NT MAXP blocks), otherwise every pass
 // re-reads them from global memory.
 //
 // A round of the water-filling caps the still-active blocks with
@@ -856,17 +857,17 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // its cap mask (s_j >= thr_min) to capmask, so the fill kernel reads the
 // score only of kept blocks that are not capped.
 // ---------------------------------------------------------------------------
-constexpr int kSipThreads = 512;
-constexpr int kSipPairsPerPass = kSipThreads;            // block pairs per pass
-constexpr int kSipMaxPairs = 32;                         // register-resident rows: M <= 32768
-
-template <int MAXP>
-__global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
+// NT threads per row (256 or 512): with fewer threads the per-round work
+// that every wave repeats (the threshold, the block reduction, its barriers)
+// is shared by fewer waves, at the cost of more scores held per thread.
+template <int NT, int MAXP>
+__global__ __launch_bounds__(NT) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
     uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
-    __shared__ double redd[kSipThreads / 64];
-    __shared__ int redi[kSipThreads / 64];
+    constexpr int kSipPairsPerPass = NT;                 // block pairs per pass
+    __shared__ double redd[NT / 64];
+    __shared__ int redi[NT / 64];
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
@@ -884,9 +885,14 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     };
     // register copies of the thread's pairs (two plain arrays so that they
     // stay in registers)
+    // (at most 32 floats each: longer arrays the compiler leaves in scratch
+    // memory)
+    static_assert(MAXP <= 32, "register-resident pairs per thread");
     float sx[MAXP > 0 ? MAXP : 1], sy[MAXP > 0 ? MAXP : 1];
+    auto get_pair = [&](int k) { return make_float2(sx[k], sy[k]); };
+    auto set_pair = [&](int k, float2 v) { sx[k] = v.x; sy[k] = v.y; };
     auto pair_at = [&](int k) {
-        if constexpr (MAXP > 0) return make_float2(sx[k], sy[k]);
+        if constexpr (MAXP > 0) return get_pair(k);
         else return load_pair(tid + k * kSipPairsPerPass);
     };
 
@@ -904,8 +910,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         for (int k = 0; k < MAXP; ++k) {
             const int i = tid + k * kSipPairsPerPass;
             const float2 v = (k < npass) ? load_pair(i) : make_float2(-1.0f, -1.0f);
-            sx[k] = v.x;
-            sy[k] = v.y;
+            set_pair(k, v);
             add_score(v.x, 2 * i);
             add_score(v.y, 2 * i + 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -961,8 +966,9 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
             if (__builtin_amdgcn_ballot_w64(vmax >= thr) != 0) {
 #pragma unroll
                 for (int k = 0; k < MAXP; ++k) {
-                    test(sx[k]);
-                    test(sy[k]);
+                    const float2 v = get_pair(k);
+                    test(v.x);
+                    test(v.y);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -989,7 +995,8 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
                 float m = -1.0f;
 #pragma unroll
                 for (int k = 0; k < MAXP; ++k) {
-                    float x = sx[k], y = sy[k];
+                    const float2 v = get_pair(k);
+                    float x = v.x, y = v.y;
                     asm volatile("" : "+v"(x), "+v"(y));
                     m = x < thr_min ? fmaxf(m, x) : m;
                     m = y < thr_min ? fmaxf(m, y) : m;
@@ -1005,9 +1012,10 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     const int64_t h = bidx % H;
     const int64_t b = bidx / H;
     int kept = 0;
-    // Pass k covers blocks [1024 k, 1024 k + 1024); wave w's lanes hold the
-    // pairs of blocks [1024 k + 128 w, +128), i.e. mask words 16 k + 2 w and
-    // 16 k + 2 w + 1, whose bits interleave the even- and odd-block ballots.
+    // Pass k covers blocks [2 NT k, 2 NT (k + 1)); wave w's lanes hold the
+    // pairs of blocks [2 NT k + 128 w, +128), i.e. mask words NT k / 32 + 2 w
+    // and NT k / 32 + 2 w + 1, whose bits interleave the even- and odd-block
+    // ballots.
     auto draw = [&](int k, float2 v) {
         const int i = tid + k * kSipPairsPerPass;
         double u0 = 1.0, u1 = 1.0;
@@ -1018,7 +1026,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
         const uint64_t ke = __ballot(keep0), ko = __ballot(keep1);
         const uint64_t ce = __ballot(cap0), co = __ballot(cap1);
         if (lane == 0) {
-            const int w0 = 16 * k + 2 * wave;
+            const int w0 = (NT / 32) * k + 2 * wave;
             if (w0 < words) {
                 km[w0] = interleave_bits(static_cast<uint32_t>(ke), static_cast<uint32_t>(ko));
                 cm[w0] = interleave_bits(static_cast<uint32_t>(ce), static_cast<uint32_t>(co));
@@ -1033,7 +1041,7 @@ __global__ __launch_bounds__(kSipThreads) void sip_count_kernel(
     if constexpr (MAXP > 0) {
 #pragma unroll
         for (int k = 0; k < MAXP; ++k) {
-            if (k < npass) draw(k, make_float2(sx[k], sy[k]));
+            if (k < npass) draw(k, get_pair(k));
             // one pair's Philox at a time: keeps the register count low
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1295,17 +1303,21 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
                             int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
                             SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
-    const int64_t npass = ((M + 1) / 2 + kSipPairsPerPass - 1) / kSipPairsPerPass;
+    // 512 threads per row, the scores of up to 32 pairs per thread in
+    // registers (rows of up to 32,768 blocks); longer rows re-read their
+    // scores every pass. (Fewer threads per row, e.g. 320 at 30 pairs each
+    // for the Wan2.1-like rows, was measured slower: 5.6 against 3.8 ms.)
+    const int64_t npass = ((M + 1) / 2 + 511) / 512;
     return launch_checked([&] {
-#define ABSA_SIP_LAUNCH(MP)                                                                      \
-    hipLaunchKernelGGL(sip_count_kernel<MP>, dim3(rows), dim3(kSipThreads), 0, s, scores, H, QB, \
+#define ABSA_SIP_LAUNCH(NT, MP)                                                                  \
+    hipLaunchKernelGGL((sip_count_kernel<NT, MP>), dim3(rows), dim3(NT), 0, s, scores, H, QB,   \
                        M, budget, seed, capmask, keepmask, rowinfo, counts, status)
-        if (npass <= 8) ABSA_SIP_LAUNCH(8);
-        else if (npass <= 16) ABSA_SIP_LAUNCH(16);
-        else if (npass <= 20) ABSA_SIP_LAUNCH(20);
-        else if (npass <= 24) ABSA_SIP_LAUNCH(24);
-        else if (npass <= kSipMaxPairs) ABSA_SIP_LAUNCH(kSipMaxPairs);
-        else ABSA_SIP_LAUNCH(0);
+        if (npass <= 8) ABSA_SIP_LAUNCH(512, 8);
+        else if (npass <= 16) ABSA_SIP_LAUNCH(512, 16);
+        else if (npass <= 20) ABSA_SIP_LAUNCH(512, 20);
+        else if (npass <= 24) ABSA_SIP_LAUNCH(512, 24);
+        else if (npass <= 32) ABSA_SIP_LAUNCH(512, 32);
+        else ABSA_SIP_LAUNCH(512, 0);
 #undef ABSA_SIP_LAUNCH
     });
 }
