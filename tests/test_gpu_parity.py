@@ -306,6 +306,26 @@ def test_sip_rounding_edges_bit_exact(K):
     check_plan_exact(plan.export(), ref, f"edge rows K={K}")
 
 
+def test_fill_queue_many_uncapped_blocks():
+    """Near-flat scores and a 50% budget: nothing is capped, so about half of
+    each row's blocks are kept with p < 1 and each needs its own logarithm.
+    The fill kernel queues such blocks per wave and finishes them 64 at a
+    time; here every wave's queue fills and is flushed many times, across
+    mask words and chunks. The plan must match the oracle's bit for bit."""
+    rng = np.random.default_rng(77)
+    B, H, N, d = 1, 2, 20480, 128            # M = 5120: 80 mask words, two 64-word waves
+    M, QB = N // 4, (N + 127) // 128
+    s = rng.uniform(0.5, 1.5, size=(B, H, QB, M))
+    s32 = (s / s.sum(axis=-1, keepdims=True)).astype(np.float32)
+    budget = M // 2
+    seed = synth.sip_seed(3)
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, budget, seed)
+    ref = oracle.plan_from_scores(s32, B, H, N, d, budget, seed)
+    gp = plan.export()
+    assert (ref.p < 1.0).mean() > 0.9               # the queued path dominates
+    check_plan_exact(gp, ref, "many uncapped")
+
+
 def test_plan_mismatch_and_bad_scores():
     q, k, v = (x.to(DEV) for x in _inputs(B=1, H=1, N=512, d=64, seed=9))
     plan = absa.absa_plan_create(q, k, 10, 1)
