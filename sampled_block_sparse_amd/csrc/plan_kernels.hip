@@ -276,8 +276,8 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
 // KV blocks of the head. This is a dense contraction (centroids x mean keys,
 // per head) that must be accurate to 1e-4 relative; it runs on the int8 MFMA
 // (32x32x32) on block floating point forms of both operands (three int8
-// digits per value, one exponent per mean key and per pair of centroid
-// slots), summing the six digit products of weight >= 2^16 in int32
+// digits per value, one exponent per mean key and one for a wave's 32
+// centroid slots), summing the six digit products of weight >= 2^16 in int32
 // accumulators (exact) and combining them in fp32; the result carries about
 // 2^-21 of the dot product's scale. A wave owns 32 centroid slots (32/CP
 // query blocks of CP slots; slots past C have weight 0) against 64-key tiles
@@ -352,7 +352,6 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     static_assert(SLOTS % 256 == 0, "tile slots must split evenly over the threads");
     __shared__ __align__(16) int8_t ks[2][3 * PL];
     __shared__ int kxs[2][TK];                      // exponents of the tile's mean keys
-    __shared__ int slot_exp[kScoreWaves][32];       // centroid exponents, per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -374,6 +373,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     const bool slot_ok = (my_r < QB) && (my_m < C);
     typedef int intx4 __attribute__((ext_vector_type(4)));
     intx4 a2[NSTEP], a1[NSTEP], a0[NSTEP];
+    float rowf;
     {
         const float* src = cent + ((bh * QB + my_r) * C + my_m) * D;
         float amax = 0.0f;
@@ -383,13 +383,14 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             for (int e = 0; e < 16; ++e)
                 amax = fmaxf(amax, slot_ok ? fabsf(src[st * 32 + half * 16 + e]) : 0.0f);
         }
-        // one exponent for the slot pair (s, s^4): the two accumulator rows a
-        // lane holds for element k lie in the two halves of the block, so
-        // each row factor is then the same for the whole wave
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        // one exponent for the wave's 32 slots (query blocks r0 .. r0 + 32/CP):
+        // the row factor is then one scalar, folded into each key's factor
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         const int ex = bfp_exponent(amax);
-        if (half == 0) slot_exp[wave][col] = ex;
+        // the log2-domain scale times 2^(e_c - 28): the digit sums carry
+        // 2^(44 - e_c - e_k), and the combination below 2^-16
+        rowf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ldexpf(scale_log2, ex - 28))));
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             int8_t h2[16], h1[16], h0[16];
@@ -413,15 +414,6 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     auto part_index = [&](int slot) {
         return ((bh * QB + r0 + slot / CP) * C + slot % CP) * nchunks;
     };
-    // Per-row factor: the log2-domain scale times 2^(e_slot - 28) (the digit
-    // sums carry 2^(44 - e_c - e_k), and the combination below 2^-16); the
-    // same in both halves (slot pairs share the exponent), so it is held in
-    // scalar registers.
-    floatx16 rowf;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-        rowf[k] = __int_as_float(__builtin_amdgcn_readfirstlane(
-            __float_as_int(ldexpf(scale_log2, slot_exp[wave][(k >> 2) * 8 + (k & 3)] - 28))));
 
     const int8_t* kb = kq + bh * M * 3 * D;
     const int* kxb = kx + bh * M;
@@ -464,16 +456,17 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     // Logit of accumulator row k, up to the key's factor: the six digit
     // products of weight >= 2^16 (X2Y2; X2Y1 + X1Y2; X2Y0 + X1Y1 + X0Y2)
     // combined as 2^16 P22 + (2^8 P21 + P20) (the bracket is exact in int32:
-    // |P21| <= 2^21, |P20| < 2^23) times the row factor. The logit is this
-    // times 2^(key exponent); the dropped products are below 2^-21 of the
-    // dot product's scale.
+    // |P21| <= 2^21, |P20| < 2^23). The logit is this times key_factor (the
+    // row factor times 2^(key exponent)); the dropped products are below
+    // 2^-21 of the largest |c| |k| of the wave's centroids.
     auto combine = [&](const intx16& i22, const intx16& i21, const intx16& i20,
-                       const floatx16& rowf, int k) __attribute__((always_inline)) {
+                       int k) __attribute__((always_inline)) {
         const int lo = (i21[k] << 8) + i20[k];
-        return fmaf(static_cast<float>(i22[k]), 65536.0f, static_cast<float>(lo)) * rowf[k];
+        return fmaf(static_cast<float>(i22[k]), 65536.0f, static_cast<float>(lo));
     };
+    // row factor times 2^(key exponent): the logit is combine(...) times this
     auto key_factor = [&](int buf, int key) __attribute__((always_inline)) {
-        return ldexpf(1.0f, kxs[buf][key]);
+        return ldexpf(rowf, kxs[buf][key]);
     };
     // One subtile's digit products (subtile sb of buffer buf) into o22/o21/o20,
     // with item(k) (the VALU work of row k of the previous subtile) spread
@@ -542,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                 const float cf = key_factor(buf, col);
                 pre();
                 phase(buf, 1, xb22, xb21, xb20,
-                      [&](int k) { item(xa22, xa21, xa20, rowf, cf, k); });
+                      [&](int k) { item(xa22, xa21, xa20, cf, k); });
                 post(2 * u, xa22, xa21, xa20, cf);
             }
             // key factor of subtile 2u+1, read before the barrier after which
@@ -553,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             if (2 * u + 1 < nsub) {
                 pre();
                 phase(buf ^ 1, 0, xa22, xa21, xa20,
-                      [&](int k) { item(xb22, xb21, xb20, rowf, cf1, k); });
+                      [&](int k) { item(xb22, xb21, xb20, cf1, k); });
                 post(2 * u + 1, xb22, xb21, xb20, cf1);
             }
         }
@@ -594,14 +587,14 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             const bool ok = t0 * kScoreTile + col < M;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float x = ok ? combine(i22, i21, i20, rowf, i) * cf : -INFINITY;
+                const float x = ok ? combine(i22, i21, i20, i) * cf : -INFINITY;
                 rebase(i, x);
                 zs[i] += __builtin_amdgcn_exp2f(x + nref[i]);
             }
         };
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
-                        const floatx16& rf, float cf, int k) __attribute__((always_inline)) {
-            dv[k] = fmaf(combine(i22, i21, i20, rf, k), cf, nref[k]);
+                        float cf, int k) __attribute__((always_inline)) {
+            dv[k] = fmaf(combine(i22, i21, i20, k), cf, nref[k]);
             over = over || dv[k] > 0.0f;
             // pinned here, between the MFMAs: the compiler would otherwise
             // sink the whole computation past them, next to its use
@@ -669,9 +662,9 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         }
         float pr[RPW];
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
-                        const floatx16& rowf, float cf, int k) __attribute__((always_inline)) {
+                        float cf, int k) __attribute__((always_inline)) {
             pr[slot_of(k) / CP] +=
-                __builtin_amdgcn_exp2f(fmaf(combine(i22, i21, i20, rowf, k), cf, bias[k]));
+                __builtin_amdgcn_exp2f(fmaf(combine(i22, i21, i20, k), cf, bias[k]));
         };
         auto pre = [&]() __attribute__((always_inline)) {
 #pragma unroll
