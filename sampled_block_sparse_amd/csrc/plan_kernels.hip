@@ -142,7 +142,10 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
     constexpr int QS = D + QStore<T>::kPad;
     constexpr int DH = D / 2;                           // channels per half
     __shared__ T qs[kQueryBlock * QS];
-    __shared__ __align__(16) double ct[D][NC];          // centroids, transposed
+    // centroids, transposed; rows padded to NC + 2 doubles (80 or 144 bytes,
+    // still 16-byte aligned for the broadcast reads) so that lanes walking
+    // the channels of one cluster spread over the banks
+    __shared__ __align__(16) double ct[D][NC + 2];
     __shared__ double part[NC][kQueryBlock];            // dot products over channel half 1
     __shared__ double cc[NC];                           // |c_m|^2
     __shared__ int assign[kQueryBlock], rank_in_wave[kQueryBlock];
