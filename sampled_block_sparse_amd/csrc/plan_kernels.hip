@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
     constexpr int NC = 2 * CH;                          // cluster slots
     constexpr int QS = D + QStore<T>::kPad;
     constexpr int DH = D / 2;                           // channels per half
-    __shared__ T qs[kQueryBlock * QS];
+    __shared__ __align__(16) T qs[kQueryBlock * QS];
     // centroids, transposed; rows padded to NC + 2 doubles (80 or 144 bytes,
     // still 16-byte aligned for the broadcast reads) so that lanes walking
     // the channels of one cluster spread over the banks
@@ -163,9 +163,20 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
     const int lane = tid & 63, wave = tid >> 6;
     const T* qrow = q + (bh * N + lo) * D;
 
-    for (int e = tid; e < n * D; e += blockDim.x) {
-        const int i = e / D, dd = e - i * D;
-        qs[i * QS + dd] = qrow[e];
+    // 16-byte global loads, stored as four 4-byte words (the padded LDS rows
+    // are 4-byte aligned; a row of D values is a whole number of 16 bytes)
+    {
+        constexpr int V = 16 / static_cast<int>(sizeof(T));    // values per 16 bytes
+        const uint4* src = reinterpret_cast<const uint4*>(qrow);
+        for (int e = tid; e < n * (D / V); e += blockDim.x) {
+            const int i = e / (D / V), c = (e - i * (D / V)) * V;
+            const uint4 u = src[e];
+            uint32_t* dst = reinterpret_cast<uint32_t*>(qs + i * QS + c);
+            dst[0] = u.x;
+            dst[1] = u.y;
+            dst[2] = u.z;
+            dst[3] = u.w;
+        }
     }
     __syncthreads();
     for (int e = tid; e < D * NC; e += blockDim.x) {
