@@ -252,21 +252,32 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
             members[pos] = tid;
         }
         __syncthreads();
-        // Update: each (cluster, channel) pair owned by one thread.
-        for (int e = tid; e < ceff * D; e += blockDim.x) {
-            const int m = e / D, dd = e - m * D;
+        // Update: each (cluster, channel pair) owned by one thread: one member
+        // index read serves both channels (the sums are exact in any order).
+        for (int e = tid; e < ceff * (D / 2); e += blockDim.x) {
+            const int m = e / (D / 2), dd = (e - m * (D / 2)) * 2;
             const int cnt = counts[m];
             if (cnt) {
-                // four independent partial sums (the sum is exact in any order)
+                // four independent partial sums per channel
                 const int* mem = members + offs[m];
-                double s4[4] = {0.0, 0.0, 0.0, 0.0};
+                double sa[4] = {0.0, 0.0, 0.0, 0.0}, sb[4] = {0.0, 0.0, 0.0, 0.0};
                 int k = 0;
                 for (; k + 4 <= cnt; k += 4) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) s4[u] += QStore<T>::get(&qs[mem[k + u] * QS + dd]);
+                    for (int u = 0; u < 4; ++u) {
+                        const T* qp = &qs[mem[k + u] * QS + dd];
+                        sa[u] += QStore<T>::get(qp);
+                        sb[u] += QStore<T>::get(qp + 1);
+                    }
                 }
-                for (; k < cnt; ++k) s4[0] += QStore<T>::get(&qs[mem[k] * QS + dd]);
-                ct[dd][m] = ((s4[0] + s4[1]) + (s4[2] + s4[3])) / static_cast<double>(cnt);
+                for (; k < cnt; ++k) {
+                    const T* qp = &qs[mem[k] * QS + dd];
+                    sa[0] += QStore<T>::get(qp);
+                    sb[0] += QStore<T>::get(qp + 1);
+                }
+                const double nm = static_cast<double>(cnt);
+                ct[dd][m] = ((sa[0] + sa[1]) + (sa[2] + sa[3])) / nm;
+                ct[dd + 1][m] = ((sb[0] + sb[1]) + (sb[2] + sb[3])) / nm;
             }
         }
         __syncthreads();
