@@ -34,6 +34,7 @@ CASES = {
     "small10": (dict(name="small"), ("pct", 10)),
     "ragged_d128": (dict(B=2, H=3, N=1000, d=128, seed=5), ("pct", 10)),
     "ragged_d64_f32": (dict(B=1, H=2, N=1340, d=64, dtype="f32", seed=6), ("pct", 20)),
+    "ragged_d128_f32": (dict(B=1, H=2, N=700, d=128, dtype="f32", seed=8), ("pct", 15)),
     "short_rows": (dict(B=1, H=2, N=200, d=128, seed=7), ("blocks", 3)),
 }
 
