@@ -792,19 +792,6 @@ __device__ __forceinline__ void sip_uniform_pair(uint64_t seed, int64_t b, int64
     u1 = static_cast<double>(((static_cast<uint64_t>(c[2]) << 32) | c[3]) >> 11) * 0x1.0p-53;
 }
 
-// Bit k of a goes to bit 2k, bit k of b to bit 2k+1 (32 bits each).
-__device__ __forceinline__ uint64_t interleave_bits(uint32_t a, uint32_t b) {
-    auto spread = [](uint64_t x) {
-        x = (x | (x << 16)) & 0x0000FFFF0000FFFFull;
-        x = (x | (x << 8)) & 0x00FF00FF00FF00FFull;
-        x = (x | (x << 4)) & 0x0F0F0F0F0F0F0F0Full;
-        x = (x | (x << 2)) & 0x3333333333333333ull;
-        x = (x | (x << 1)) & 0x5555555555555555ull;
-        return x;
-    };
-    return spread(a) | (spread(b) << 1);
-}
-
 // floor(s * 2^52) of an fp32 score in [0, 1], as an exact fp64 integer. Sums
 // of such integers below 2^53 are exact in fp64 in any order, which is the
 // order-free fixed-point arithmetic the sampler's rule asks for.
@@ -879,7 +866,7 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // that every wave repeats (the threshold, the block reduction, its barriers)
 // is shared by fewer waves, at the cost of more scores held per thread.
 template <int NT, int MAXP>
-__global__ __launch_bounds__(NT) void sip_count_kernel(
+__global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
     uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
@@ -1031,9 +1018,8 @@ __global__ __launch_bounds__(NT) void sip_count_kernel(
     const int64_t b = bidx / H;
     int kept = 0;
     // Pass k covers blocks [2 NT k, 2 NT (k + 1)); wave w's lanes hold the
-    // pairs of blocks [2 NT k + 128 w, +128), i.e. mask words NT k / 32 + 2 w
-    // and NT k / 32 + 2 w + 1, whose bits interleave the even- and odd-block
-    // ballots.
+    // pairs of blocks [2 NT k + 128 w, +128) (i_0 = NT k + 64 w is the pair of
+    // lane 0), i.e. mask words w0 = NT k / 32 + 2 w and w0 + 1.
     auto draw = [&](int k, float2 v) {
         const int i = tid + k * kSipPairsPerPass;
         double u0 = 1.0, u1 = 1.0;
@@ -1041,17 +1027,24 @@ __global__ __launch_bounds__(NT) void sip_count_kernel(
         const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
         const bool keep0 = 2 * i < M32 && u0 < sip_p(cap0, ri, v.x);
         const bool keep1 = 2 * i + 1 < M32 && u1 < sip_p(cap1, ri, v.y);
-        const uint64_t ke = __ballot(keep0), ko = __ballot(keep1);
-        const uint64_t ce = __ballot(cap0), co = __ballot(cap1);
+        // Bit b of word w0 is block 2 (i_0 + b/2) + (b & 1), held by lane b/2
+        // (of word w0 + 1: lane 32 + b/2). Lane b fetches that lane's four
+        // bits and the ballots give the words in block order.
+        const int packed = (keep0 ? 1 : 0) | (keep1 ? 2 : 0) | (cap0 ? 4 : 0) | (cap1 ? 8 : 0);
+        const int f_lo = __builtin_amdgcn_ds_bpermute((lane >> 1) << 2, packed);
+        const int f_hi = __builtin_amdgcn_ds_bpermute((32 + (lane >> 1)) << 2, packed);
+        const int sh = lane & 1;
+        const uint64_t k_lo = __ballot((f_lo >> sh) & 1), k_hi = __ballot((f_hi >> sh) & 1);
+        const uint64_t c_lo = __ballot((f_lo >> (2 + sh)) & 1), c_hi = __ballot((f_hi >> (2 + sh)) & 1);
         if (lane == 0) {
             const int w0 = (NT / 32) * k + 2 * wave;
             if (w0 < words) {
-                km[w0] = interleave_bits(static_cast<uint32_t>(ke), static_cast<uint32_t>(ko));
-                cm[w0] = interleave_bits(static_cast<uint32_t>(ce), static_cast<uint32_t>(co));
+                km[w0] = k_lo;
+                cm[w0] = c_lo;
             }
             if (w0 + 1 < words) {
-                km[w0 + 1] = interleave_bits(static_cast<uint32_t>(ke >> 32), static_cast<uint32_t>(ko >> 32));
-                cm[w0 + 1] = interleave_bits(static_cast<uint32_t>(ce >> 32), static_cast<uint32_t>(co >> 32));
+                km[w0 + 1] = k_hi;
+                cm[w0 + 1] = c_hi;
             }
         }
         kept += (keep0 ? 1 : 0) + (keep1 ? 1 : 0);
