@@ -154,15 +154,16 @@ absa_status absa_plan_export_intermediate(absa_plan plan, absa_intermediate whic
  * softmax over the keys of the plan's KV blocks of that row with logit
  * z = q.k / sqrt(d) + logw(block), times V. o: device [B, H, N, d] of
  * dtype. A row whose plan holds no block gets zeros. bf16 MFMA products,
- * fp32 accumulation and softmax. ABSA_ERR_PLAN_MISMATCH if the plan's
- * (B, H, N, d) differ. */
+ * fp32 accumulation and softmax. q, k and v must be finite: a NaN or an
+ * infinity among them gives an unspecified output (no error is reported).
+ * ABSA_ERR_PLAN_MISMATCH if the plan's (B, H, N, d) differ. */
 absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k,
                                   const void* v, void* o, absa_dtype dtype,
                                   int64_t B, int64_t H, int64_t N, int64_t d,
                                   void* hip_stream);
 
 /* Dense softmax(Q K^T / sqrt(d)) V with the same tiles and arithmetic as
- * absa_sparse_attention (the comparator). */
+ * absa_sparse_attention (the comparator); q, k and v must be finite. */
 absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
                                  absa_dtype dtype, int64_t B, int64_t H, int64_t N,
                                  int64_t d, void* hip_stream);

@@ -33,6 +33,20 @@ COMMON = [
 ]
 
 
+# Per-source additions. The attention kernels never see a NaN they must
+# propagate (a NaN input gives an unspecified output), so fmax there needs no
+# quieting of its operands: without this every max of MFMA accumulators is
+# preceded by two canonicalising v_max ops and every max with -inf is kept.
+EXTRA = {
+    "attn_kernels.hip": ["-fno-honor-nans"],
+}
+
+
+def source_flags(src: str):
+    """Compiler flags of one source file (COMMON plus its own additions)."""
+    return [*COMMON, *EXTRA.get(src, [])]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -60,7 +74,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *source_flags(src), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"

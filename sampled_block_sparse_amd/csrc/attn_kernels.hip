@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         base = P.rowptr[row];
         cnt = P.rowptr[row + 1] - base;
     }
-    const int64_t ntiles = (cnt + kTileBlocks - 1) / kTileBlocks;
     const int cnt32 = static_cast<int>(cnt);              // <= M < 2^19
+    const int ntiles = (cnt32 + kTileBlocks - 1) / kTileBlocks;
 
     // ---- the wave's queries as the B operand of S^T = K Q^T ----
     const int64_t my_q = q0 + wave * 32 + col;
@@ -213,12 +213,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // Plan entries of one tile: lane j < 16 holds block id j of the tile and
     // lane 16 + j the bits of its fp32 log-weight (one coalesced load per
     // tile; entries past the row's end repeat its last entry).
-    auto load_plan = [&](int64_t t) -> int {
+    const int* plan_src = DENSE ? nullptr
+                                : ((lane & 16) ? reinterpret_cast<const int*>(P.logw) : P.idx) + base;
+    auto load_plan = [&](int t) -> int {
         if (DENSE) return 0;
-        const int64_t gb = t * kTileBlocks + (lane & 15);
-        const int64_t e = base + ((gb < cnt) ? gb : (cnt - 1));
-        const int* src = (lane & 16) ? reinterpret_cast<const int*>(P.logw) + e : P.idx + e;
-        return *src;
+        const int gb = t * kTileBlocks + (lane & 15);
+        return plan_src[(gb < cnt32) ? gb : (cnt32 - 1)];
     };
     // Direct gather of K or V of tile T into buffer b. Wave w fills the 1 KB
     // LDS chunks w*CPW .. w*CPW+CPW-1 of the tile; lane l's 16 bytes land at
@@ -226,11 +226,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // lane loads the logical column that the swizzle puts there.
     const int lkey = lane / (ROWB / 16);
     const int lcol = lane % (ROWB / 16);
-    auto gather = [&](auto is_v, auto b, int ivt, int64_t T) {
+    auto gather = [&](auto is_v, auto b, int ivt, int T32) {
         constexpr bool ISV = decltype(is_v)::value;
         const char* gsrc = ISV ? vbase : kbase;
         uint16_t* dst = ISV ? Vbuf(b) : Kbuf(b);
-        const int T32 = static_cast<int>(T);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int ch = wave * CPW + i;
@@ -253,10 +252,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         }
     };
     // Log-weights of tile T (log2 units; -inf past the row's end) into buffer b.
-    auto write_lws = [&](auto b, int ivt, int64_t T) {
+    auto write_lws = [&](auto b, int ivt, int T) {
         if (wave == 0 && (lane >> 4) == 1) {
             const int j = lane - 16;
-            const bool ok = static_cast<int>(T) * kTileBlocks + j < cnt32;
+            const bool ok = T * kTileBlocks + j < cnt32;
             const float lw = DENSE ? 0.0f : __int_as_float(ivt) * kLog2e;
             Lbuf(b)[j] = ok ? lw : -INFINITY;
         }
@@ -393,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // t, Snext receives S^T of tile t+1. The loop runs two steps per
     // iteration with the roles of the two accumulator sets swapped, so no
     // registers are copied.
-    auto step = [&](auto b, int64_t t, SAcc& Scur, SAcc& Snext) {
+    auto step = [&](auto b, int t, SAcc& Scur, SAcc& Snext) {
         constexpr int buf = decltype(b)::value;
         const IntC<buf ^ 1> nb{};
         if (t + 2 < ntiles) gather(IntC<0>{}, b, iv2, t + 2);
@@ -494,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
         iv2 = ivn;
     };
     SAcc Sb;
-    for (int64_t t = 0; t < ntiles; t += 2) {
+    for (int t = 0; t < ntiles; t += 2) {
         step(IntC<0>{}, t, Sa, Sb);
         if (t + 1 < ntiles) step(IntC<1>{}, t + 1, Sb, Sa);
     }

@@ -17,7 +17,8 @@ FILES = ["plan_kernels.hip", "attn_kernels.hip"]
 
 
 def _assembly(src, out):
-    flags = [f for f in absa_build.COMMON if f not in ("-fPIC", "-Wall", "-Wno-unused-function")]
+    flags = [f for f in absa_build.source_flags(src)
+             if f not in ("-fPIC", "-Wall", "-Wno-unused-function")]
     cmd = [absa_build.hipcc(), *flags, "--cuda-device-only", "-S",
            os.path.join(absa_build.CSRC, src), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
