@@ -123,7 +123,7 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
 // V tiles are stored row-major [key][channel] with 64-byte segments XOR-ed
 // by a function of the key row, so that the transpose reads of 4 consecutive
 // keys x 64 bytes hit distinct LDS banks.
-template <int D> __device__ __forceinline__ int vseg_swizzle(int key) {
+template <int D> __device__ __forceinline__ constexpr int vseg_swizzle(int key) {
     return (D == 128) ? (key & 3) : ((key >> 1) & 1);
 }
 
@@ -131,7 +131,7 @@ template <int D> __device__ __forceinline__ int vseg_swizzle(int key) {
 // column c of key row `key` sits at column c ^ kcol_swizzle(key), so that the
 // K operand reads (one column of 16 consecutive keys per 16 lanes) hit
 // distinct LDS banks.
-template <int D> __device__ __forceinline__ int kcol_swizzle(int key) {
+template <int D> __device__ __forceinline__ constexpr int kcol_swizzle(int key) {
     return (D == 128) ? (key & 15) : ((key >> 1) & 7);
 }
 
@@ -162,11 +162,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     constexpr uint32_t BLOCK_BYTES = kKvBlock * ROWB;
     constexpr int CPW = kTileKeys * ROWB / 1024 / 4;   // 1 KB gather chunks per wave
     constexpr int KPC = 1024 / ROWB;            // key rows per chunk
-    __shared__ __align__(16) uint16_t Ks0[kTileKeys * D], Ks1[kTileKeys * D];
+    // the two K buffers are one array, so a K operand address is one
+    // loop-invariant register plus an immediate offset for buffer and key half
+    __shared__ __align__(16) uint16_t Ks[2][kTileKeys * D];
     __shared__ __align__(16) uint16_t Vs0[kTileKeys * D], Vs1[kTileKeys * D];
     __shared__ float lws0[kTileBlocks], lws1[kTileBlocks];
     // Buffer b of each kind; b is a compile-time constant at every use.
-    auto Kbuf = [&](auto b) -> uint16_t* { if constexpr (decltype(b)::value) return Ks1; else return Ks0; };
+    auto Kbuf = [&](auto b) -> uint16_t* { return Ks[decltype(b)::value]; };
     auto Vbuf = [&](auto b) -> uint16_t* { if constexpr (decltype(b)::value) return Vs1; else return Vs0; };
     auto Lbuf = [&](auto b) -> float* { if constexpr (decltype(b)::value) return lws1; else return lws0; };
 
@@ -226,6 +228,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // lane loads the logical column that the swizzle puts there.
     const int lkey = lane / (ROWB / 16);
     const int lcol = lane % (ROWB / 16);
+    // With one block per chunk (d = 128) a chunk's block address goes into
+    // the load's scalar base (scalar arithmetic) and each lane adds a fixed
+    // offset: that of its key row within the block and its swizzled column.
+    // The offsets depend on the chunk only through i (the wave's chunks
+    // start at a multiple of 16 keys, the swizzle period), so they are
+    // computed once.
+    uint32_t goff[2][CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int key = (wave * CPW + i) * KPC + lkey;
+        goff[0][i] = static_cast<uint32_t>((key & 3) * ROWB + (lcol ^ kcol_swizzle<D>(key)) * 16);
+        goff[1][i] = static_cast<uint32_t>((key & 3) * ROWB + (lcol ^ (vseg_swizzle<D>(key) << 2)) * 16);
+        if constexpr (KPC == 4 && !DENSE) asm volatile("" : "+v"(goff[0][i]), "+v"(goff[1][i]));
+    }
     auto gather = [&](auto is_v, auto b, int ivt, int T32) {
         constexpr bool ISV = decltype(is_v)::value;
         const char* gsrc = ISV ? vbase : kbase;
@@ -233,13 +249,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int ch = wave * CPW + i;
+            if constexpr (KPC == 4 && !DENSE) {
+                const uint32_t blk = static_cast<uint32_t>(__builtin_amdgcn_readlane(ivt, ch));
+                load_to_lds(gsrc + blk * BLOCK_BYTES, goff[ISV][i], dst + ch * 512);
+                continue;
+            }
             const int key = ch * KPC + lkey;                // key of the tile, 0..63
             int blk;
             if (DENSE) {
                 const int gb = T32 * kTileBlocks + (key >> 2);
                 blk = (gb < cnt32) ? gb : (cnt32 - 1);
-            } else if (KPC == 4) {
-                blk = __builtin_amdgcn_readlane(ivt, ch);   // the chunk is one block
             } else {
                 const int b0 = __builtin_amdgcn_readlane(ivt, 2 * ch);
                 const int b1 = __builtin_amdgcn_readlane(ivt, 2 * ch + 1);
@@ -278,12 +297,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     };
 
     // K operand of MFMA step s2 for key half kb: key row kb*32 + col,
-    // logical 16-byte column 2*s2 + half.
-    const int kswz0 = kcol_swizzle<D>(col), kswz1 = kcol_swizzle<D>(32 + col);
+    // logical 16-byte column 2*s2 + half. Rows col and 32 + col have the
+    // same swizzle, so the key half is an offset of 32 rows; the byte offset
+    // of each step is computed once.
+    static_assert(kcol_swizzle<D>(0) == kcol_swizzle<D>(32) && kcol_swizzle<D>(5) == kcol_swizzle<D>(37),
+                  "K swizzle period must divide 32 rows");
+    uint32_t koff[NS];
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+        koff[s2] = static_cast<uint32_t>(col * ROWB + (((2 * s2 + half) ^ kcol_swizzle<D>(col)) * 16));
+        asm volatile("" : "+v"(koff[s2]));
+    }
     auto k_operand = [&](auto b, int kb, int s2) {
-        const int key = kb * 32 + col;
-        const int pc = (2 * s2 + half) ^ (kb ? kswz1 : kswz0);
-        return *reinterpret_cast<const uint4*>(Kbuf(b) + key * D + pc * 8);
+        const char* p = reinterpret_cast<const char*>(Kbuf(b)) + kb * 32 * ROWB;
+        return *reinterpret_cast<const uint4*>(p + koff[s2]);
     };
 
     struct SAcc { floatx16 v[2]; };
