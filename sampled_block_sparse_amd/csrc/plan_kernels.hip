@@ -846,10 +846,14 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // SIP probabilities and draws [hamidun, SIP paragraph; edumints, SIP item]:
 // capped water-filling in exact fixed point (q_j = floor(s_j 2^52), exact
 // sums, IEEE double division and product), then one Poisson draw per block.
-// One workgroup of NT threads per plan row. Thread t owns the block pairs
-// (2i, 2i+1) with i = t + NT k; with MAXP > 0 it keeps their scores in
-// registers (rows of up to 2 NT MAXP blocks), otherwise every pass
-// re-reads them from global memory.
+// One workgroup of NT threads per plan row. Lane l of wave w owns the block
+// pairs (2i, 2i+1) with i = i0(w, k) + l for passes k = 0, 1, ...: with
+// MAXP > 0 the wave covers one contiguous range of 64 MAXP pairs
+// (i0 = 64 (MAXP w + k)) and keeps their scores in registers (rows of up to
+// 2 NT MAXP blocks); otherwise i0 = NT k + 64 w and every pass re-reads the
+// scores from global memory. With contiguous ranges the blocks a round caps
+// (neighbours in the video grid, hence in block order) fall in few waves,
+// and a wave with none of them skips the round's pass.
 //
 // A round of the water-filling caps the still-active blocks with
 // fl(c q_j) >= 1, i.e. q_j >= T(c) (cap_threshold), i.e. s_j >= thr(c) for
@@ -879,7 +883,8 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     uint64_t* km = keepmask + row * words;
     uint64_t* cm = capmask + row * words;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: pass offsets in scalar registers
     const int M32 = static_cast<int>(M);                  // M < 2^19
     const int npairs = (M32 + 1) / 2;
     const int npass = (npairs + kSipPairsPerPass - 1) / kSipPairsPerPass;
@@ -896,9 +901,18 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     float sx[MAXP > 0 ? MAXP : 1], sy[MAXP > 0 ? MAXP : 1];
     auto get_pair = [&](int k) { return make_float2(sx[k], sy[k]); };
     auto set_pair = [&](int k, float2 v) { sx[k] = v.x; sy[k] = v.y; };
+    // First pair of the wave's pass k (a multiple of 64): pbase + step k.
+    // Written as one base plus constants so that nothing per pass stays
+    // live (the lane's pair is one register plus an immediate; a pass lies
+    // within the row iff step k < prem).
+    constexpr int kPassStep = MAXP > 0 ? 64 : kSipPairsPerPass;
+    const int pbase = MAXP > 0 ? 64 * MAXP * wave : 64 * wave;
+    const int prem = npairs - pbase;
+    const int ibase = pbase + lane;
+    auto in_row = [&](int k) { return kPassStep * k < prem; };
     auto pair_at = [&](int k) {
         if constexpr (MAXP > 0) return get_pair(k);
-        else return load_pair(tid + k * kSipPairsPerPass);
+        else return load_pair(ibase + kPassStep * k);
     };
 
     FixedSum sum;
@@ -913,8 +927,8 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     if constexpr (MAXP > 0) {
 #pragma unroll
         for (int k = 0; k < MAXP; ++k) {
-            const int i = tid + k * kSipPairsPerPass;
-            const float2 v = (k < npass) ? load_pair(i) : make_float2(-1.0f, -1.0f);
+            const int i = ibase + kPassStep * k;
+            const float2 v = in_row(k) ? load_pair(i) : make_float2(-1.0f, -1.0f);
             set_pair(k, v);
             add_score(v.x, 2 * i);
             add_score(v.y, 2 * i + 1);
@@ -922,7 +936,7 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
         }
     } else {
         for (int k = 0; k < npass; ++k) {
-            const int i = tid + k * kSipPairsPerPass;
+            const int i = ibase + kPassStep * k;
             const float2 v = load_pair(i);
             add_score(v.x, 2 * i);
             add_score(v.y, 2 * i + 1);
@@ -1017,11 +1031,15 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     const int64_t h = bidx % H;
     const int64_t b = bidx / H;
     int kept = 0;
-    // Pass k covers blocks [2 NT k, 2 NT (k + 1)); wave w's lanes hold the
-    // pairs of blocks [2 NT k + 128 w, +128) (i_0 = NT k + 64 w is the pair of
-    // lane 0), i.e. mask words w0 = NT k / 32 + 2 w and w0 + 1.
+    // In pass k wave w's lanes hold the pairs of blocks [2 i_0, 2 i_0 + 128)
+    // (i_0 = pbase + step k, the pair of lane 0), i.e. mask words
+    // w0 = i_0 / 32 and w0 + 1. Opaque copies of the bases: the pass offsets
+    // are recomputed here, not kept live from the loads (registers).
+    int ibase_d = ibase, prem_d = prem;
+    asm volatile("" : "+v"(ibase_d), "+s"(prem_d));
+    auto in_row_d = [&](int k) { return kPassStep * k < prem_d; };
     auto draw = [&](int k, float2 v) {
-        const int i = tid + k * kSipPairsPerPass;
+        const int i = ibase_d + kPassStep * k;
         double u0 = 1.0, u1 = 1.0;
         sip_uniform_pair(seed, b, h, r, i, u0, u1);
         const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
@@ -1037,7 +1055,7 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
         const uint64_t k_lo = __ballot((f_lo >> sh) & 1), k_hi = __ballot((f_hi >> sh) & 1);
         const uint64_t c_lo = __ballot((f_lo >> (2 + sh)) & 1), c_hi = __ballot((f_hi >> (2 + sh)) & 1);
         if (lane == 0) {
-            const int w0 = (NT / 32) * k + 2 * wave;
+            const int w0 = pbase / 32 + (kPassStep / 32) * k;
             if (w0 < words) {
                 km[w0] = k_lo;
                 cm[w0] = c_lo;
@@ -1052,7 +1070,7 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     if constexpr (MAXP > 0) {
 #pragma unroll
         for (int k = 0; k < MAXP; ++k) {
-            if (k < npass) draw(k, get_pair(k));
+            if (in_row_d(k)) draw(k, get_pair(k));
             // one pair's Philox at a time: keeps the register count low
             __builtin_amdgcn_sched_barrier(0);
         }
