@@ -11,7 +11,7 @@ import oracle
 import sampled_block_sparse_amd as absa
 import synth
 from tests.gpu_util import (SCORE_REL, check_output, check_plan_exact, flips_explained,
-                            oracle_plan_of, score_error, to64)
+                            oracle_plan_of, score_error, to64, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -325,6 +325,43 @@ def test_fill_queue_many_uncapped_blocks():
     gp = plan.export()
     assert (ref.p < 1.0).mean() > 0.9               # the queued path dominates
     check_plan_exact(gp, ref, "many uncapped")
+
+
+@pytest.mark.parametrize("M", [9001, 23000, 32765, 40002])
+def test_sip_row_length_tiers(M):
+    """The SIP count kernel keeps a row's scores in registers in tiers of
+    8, 16, 20, 24 or 32 block pairs per thread and re-reads them from memory
+    for longer rows; each wave owns one contiguous range of pairs, the last
+    one partly past the row's end. These lengths take the 16-, 24- and
+    32-pair tiers and the memory path (the video layers take 20 and 32), with
+    odd M. Rows alternate between heavy-tailed scores spread over the row
+    and scores concentrated in one window (so that in later capping rounds
+    most waves skip their pass). Sampled rows must match the oracle's SIP
+    bit for bit."""
+    rng = np.random.default_rng(M)
+    N, d = 4 * M, 64
+    QB = (N + 127) // 128
+    z = rng.standard_normal((QB, M))
+    s = np.exp(1.5 * z)
+    win = rng.integers(0, M - 600, size=QB)
+    for r in range(1, QB, 2):
+        s[r] = np.exp(0.5 * z[r])
+        s[r, win[r]:win[r] + 600] *= 300.0
+    s32 = (s / s.sum(axis=-1, keepdims=True) * 0.999).astype(np.float32)[None, None]
+    budget = M // 10
+    seed = synth.sip_seed(5)
+    print(f"[sip tiers] M={M} rows={QB}", flush=True)
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, budget, seed)
+    gp = plan.export()
+    plan.destroy()
+    for r in sorted({0, 1, 2, 3, QB // 2, QB // 2 + 1, QB - 2, QB - 1}):
+        p = oracle.sip_probabilities(s32[0, 0, r], budget)
+        idx, logw, pk = oracle.sip_draw_row(p, seed, 0, 0, r)
+        lo, hi = gp["rowptr"][r], gp["rowptr"][r + 1]
+        np.testing.assert_array_equal(gp["idx"][lo:hi], idx, err_msg=f"M={M} row {r}")
+        assert np.array_equal(gp["p"][lo:hi].view(np.uint64), pk.view(np.uint64)), f"M={M} row {r}"
+        assert (ulp_diff_f32(gp["logw"][lo:hi], logw) <= 1).all(), f"M={M} row {r}"
+        assert (pk == 1.0).sum() > 0, f"M={M} row {r}: no block capped"
 
 
 def test_plan_mismatch_and_bad_scores():
