@@ -29,6 +29,10 @@ Steps, in the order the method applies them, and what pins each:
                       pinned by its published known-answer values
   sip_draw_row        [hamidun, SIP]                       pinned by inclusion
                       frequencies over many seeds
+  systematic_draw_row fixed-size design (reading of the pages' fixed budget)
+                      pinned by exact inclusion counts over a grid of U,
+                      the closed form for equal sizes, always-taken p = 1
+                      blocks and the sample size
   ht_attention_row    [hamidun, SIP and kernel paragraphs] pinned by budget 100%
                       == dense, "p = 25% counts four times" == physical key
                       duplication through library attention, Monte-Carlo
@@ -37,7 +41,9 @@ Steps, in the order the method applies them, and what pins each:
                       scaled-dot-product attention on the CPU
 """
 from .ibcs import mean_keys, kmeans_block, ibcs_scores_row, ibcs_row, query_rows
-from .sip import sip_probabilities, sip_draw_row, sip_uniforms, fixed_point_scores
+from .sip import (sip_probabilities, sip_draw_row, sip_uniforms, fixed_point_scores,
+                  systematic_uniform, systematic_sizes, systematic_select,
+                  systematic_draw_row, draw_row)
 from .philox import philox4x32_10
 from .attention import (ht_attention_row, dense_attention, dense_attention_rows,
                         ht_numerator_denominator)
@@ -46,6 +52,8 @@ from .plan import build_plan, plan_from_scores, ibcs_scores, plan_attention, Ora
 __all__ = [
     "mean_keys", "kmeans_block", "ibcs_scores_row", "ibcs_row", "query_rows",
     "sip_probabilities", "sip_draw_row", "sip_uniforms", "fixed_point_scores",
+    "systematic_uniform", "systematic_sizes", "systematic_select", "systematic_draw_row",
+    "draw_row",
     "philox4x32_10", "ht_attention_row", "dense_attention", "dense_attention_rows",
     "ht_numerator_denominator", "build_plan", "plan_from_scores", "ibcs_scores",
     "plan_attention", "OraclePlan",

@@ -15,7 +15,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .ibcs import mean_keys, kmeans_block, ibcs_scores_row, query_rows
-from .sip import sip_probabilities, sip_draw_row
+from .sip import sip_probabilities, draw_row
 
 
 @dataclass
@@ -60,8 +60,9 @@ def ibcs_scores(Q, K, n_clusters: int = 8, iters: int = 4, query_block: int = 12
     return scores, cents, wts
 
 
-def plan_from_scores(scores32, B: int, H: int, N: int, d: int, budget: int, seed: int):
-    """SIP plan from fp32 scores [B, H, QB, M]."""
+def plan_from_scores(scores32, B: int, H: int, N: int, d: int, budget: int, seed: int,
+                     sampling: str = "poisson"):
+    """SIP plan from fp32 scores [B, H, QB, M] (sampling: "poisson" or "systematic")."""
     scores32 = np.asarray(scores32, dtype=np.float32)
     QB, M = scores32.shape[2], scores32.shape[3]
     counts = np.zeros(B * H * QB, dtype=np.int64)
@@ -70,7 +71,7 @@ def plan_from_scores(scores32, B: int, H: int, N: int, d: int, budget: int, seed
         for h in range(H):
             for r in range(QB):
                 p = sip_probabilities(scores32[b, h, r], budget)
-                parts.append(sip_draw_row(p, seed, b, h, r))
+                parts.append(draw_row(p, seed, b, h, r, sampling))
                 counts[(b * H + h) * QB + r] = parts[-1][0].size
     rowptr = np.zeros(B * H * QB + 1, dtype=np.int64)
     rowptr[1:] = np.cumsum(counts)
@@ -81,11 +82,12 @@ def plan_from_scores(scores32, B: int, H: int, N: int, d: int, budget: int, seed
                       logw.astype(np.float32), p.astype(np.float64))
 
 
-def build_plan(Q, K, budget: int, seed: int, n_clusters: int = 8, iters: int = 4):
+def build_plan(Q, K, budget: int, seed: int, n_clusters: int = 8, iters: int = 4,
+               sampling: str = "poisson"):
     """Full plan: mean keys, IBCS scores, then SIP on the fp32-rounded scores."""
     B, H, N, d = Q.shape
     scores, cents, wts = ibcs_scores(Q, K, n_clusters, iters)
-    plan = plan_from_scores(scores.astype(np.float32), B, H, N, d, budget, seed)
+    plan = plan_from_scores(scores.astype(np.float32), B, H, N, d, budget, seed, sampling)
     plan.scores, plan.centroids, plan.weights = scores, cents, wts
     return plan
 

@@ -31,6 +31,18 @@ Readings where the pages are silent:
     >> 11) * 2^-53, and block j is kept iff u < p_j;
   * the Horvitz-Thompson weight 1/p enters as the logit offset
     logw = -ln(p) (natural log, fp64, rounded to fp32; +0 for p = 1).
+  * a second, fixed-size design (the pages speak of a fixed budget per query
+    block; the Poisson design meets it only in expectation): systematic
+    sampling with unequal probabilities. In fixed point with unit 2^-40,
+    P_j = floor(p_j * 2^40); C_j = P_0 + ... + P_j (exact integers); one
+    uniform U in [0, 2^40) per row, from Philox4x32-10(key = seed, counter =
+    (2^32 - 1, r, h, b)), words (x0, x1) as (hi, lo), U = (hi << 32 | lo) >> 24;
+    the points U + k 2^40 (k = 0, 1, ...) fall in the intervals [C_{j-1}, C_j),
+    and block j is taken iff its interval holds one. Block j is then taken
+    with probability exactly P_j 2^-40 (its interval is at most 2^40 long),
+    which is the p the plan records and weights by; the row takes
+    floor or ceil of sum P / 2^40 blocks, i.e. K, or K - 1 when rounding left
+    the sum just below K 2^40 and U fell in the gap.
 """
 from __future__ import annotations
 
@@ -103,3 +115,54 @@ def sip_draw_row(p: np.ndarray, seed: int, b: int, h: int, r: int):
     pk = p[keep]
     logw = np.where(pk == 1.0, 0.0, -np.log(pk)).astype(np.float32)
     return keep.astype(np.int32), logw, pk
+
+
+SYS_BITS = 40
+SYS_UNIT = 1 << SYS_BITS
+
+
+def systematic_uniform(seed: int, b: int, h: int, r: int) -> int:
+    """The row's U in [0, 2^40) for the fixed-size design."""
+    x0, x1, _, _ = philox4x32_10(np.array([0xFFFFFFFF], dtype=np.uint64), r, h, b,
+                                 seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    return int(((int(x0[0]) << 32) | int(x1[0])) >> 24)
+
+
+def systematic_sizes(p: np.ndarray) -> np.ndarray:
+    """P_j = floor(p_j * 2^40) as uint64 (p in [0, 1])."""
+    return np.floor(np.asarray(p, dtype=np.float64) * float(SYS_UNIT)).astype(np.uint64)
+
+
+def systematic_select(P: np.ndarray, U: int) -> np.ndarray:
+    """Blocks whose interval [C_{j-1}, C_j) holds a point U + k 2^40 (k >= 0)."""
+    P = np.asarray(P, dtype=np.uint64)
+    C = np.cumsum(P, dtype=np.uint64)
+    Cprev = C - P
+    U = np.uint64(U)
+
+    def points_below(x):
+        # #{k >= 0 : U + k 2^40 < x}
+        above = x > U
+        safe = np.where(above, x - U - np.uint64(1), np.uint64(0))
+        return np.where(above, (safe >> np.uint64(SYS_BITS)) + np.uint64(1), np.uint64(0))
+
+    return points_below(C) > points_below(Cprev)
+
+
+def systematic_draw_row(p: np.ndarray, seed: int, b: int, h: int, r: int):
+    """Fixed-size draw of one row: ascending kept block indices, fp32
+    log-weights -ln(P 2^-40), and the inclusion probabilities P 2^-40."""
+    P = systematic_sizes(p)
+    keep = np.nonzero(systematic_select(P, systematic_uniform(seed, b, h, r)))[0]
+    pk = P[keep].astype(np.float64) * (1.0 / SYS_UNIT)
+    logw = np.where(pk == 1.0, 0.0, -np.log(pk)).astype(np.float32)
+    return keep.astype(np.int32), logw, pk
+
+
+def draw_row(p: np.ndarray, seed: int, b: int, h: int, r: int, sampling: str = "poisson"):
+    """The row's draw under the named design ("poisson" or "systematic")."""
+    if sampling == "poisson":
+        return sip_draw_row(p, seed, b, h, r)
+    if sampling == "systematic":
+        return systematic_draw_row(p, seed, b, h, r)
+    raise ValueError(f"unknown sampling design {sampling!r}")

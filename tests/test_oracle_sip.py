@@ -124,3 +124,90 @@ def test_draw_frequencies_match_probabilities():
     var = (p * (1 - p)).sum()
     assert abs(counts.mean() - K) < 5 * np.sqrt(var / S)
     assert abs(counts.var() / var - 1) < 0.15
+
+
+# ---- fixed-size (systematic) design --------------------------------------
+
+def _u_grid(n=4096):
+    """n evenly spaced values of U covering [0, 2^40)."""
+    return [t * (oracle.sip.SYS_UNIT // n) for t in range(n)]
+
+
+def test_systematic_inclusion_counts_over_u_grid():
+    """Over U on an even grid of 4096 points, block j must be taken for
+    P_j / 2^28 of them, give or take one: its inclusion probability is
+    exactly P_j 2^-40. A wrong cumulative sum (inclusive for exclusive), an
+    off-by-one in the point count or a lost carry shows up here."""
+    p = np.array([0.3, 1.0, 0.05, 0.65, 2.0 ** -30, 0.0, 0.999999, 1.0, 0.25, 0.7500001])
+    P = oracle.systematic_sizes(p)
+    grid = _u_grid()
+    hits = np.zeros(p.size, dtype=np.int64)
+    for U in grid:
+        hits += oracle.systematic_select(P, U)
+    expect = P.astype(np.float64) / float(oracle.sip.SYS_UNIT // len(grid))
+    assert np.all(np.abs(hits - expect) <= 1.0), (hits, expect)
+    assert hits[1] == hits[7] == len(grid)            # p = 1: always taken
+    assert hits[5] == 0                                # p = 0: never
+
+
+def test_systematic_equal_sizes_closed_form():
+    """p = 1/4 on 64 blocks (sum 16 exactly): the sample is every fourth
+    block starting at floor(U / 2^38), for any U."""
+    p = np.full(64, 0.25)
+    P = oracle.systematic_sizes(p)
+    rng = np.random.default_rng(3)
+    for U in list(rng.integers(0, oracle.sip.SYS_UNIT, size=50)) + [0, oracle.sip.SYS_UNIT - 1]:
+        U = int(U)
+        sel = np.nonzero(oracle.systematic_select(P, U))[0]
+        j0 = U >> 38
+        np.testing.assert_array_equal(sel, np.arange(j0, 64, 4))
+
+
+def test_systematic_sample_size_is_the_budget():
+    """Rows from the capped water-filling (sum of p = K up to rounding):
+    every draw takes K blocks, or K - 1 / K + 1 when rounding moved the
+    fixed-point total off K 2^40, and then only if U falls in that gap."""
+    rng = np.random.default_rng(11)
+    for t in range(40):
+        M = int(rng.integers(50, 400))
+        K = int(rng.integers(1, M + 1))
+        s = rng.random(M) ** rng.uniform(1, 8)
+        s32 = (s / s.sum() * 0.999).astype(np.float32)
+        p = oracle.sip_probabilities(s32, K)
+        P = oracle.systematic_sizes(p)
+        total = int(P.sum(dtype=np.uint64))
+        idx, logw, pk = oracle.systematic_draw_row(p, 1234 + t, 0, t % 3, t)
+        lo, hi = total >> 40, -(-total >> 40)
+        assert lo <= idx.size <= hi, (idx.size, lo, hi)
+        assert K - 1 <= idx.size <= K + 1
+        assert np.all(np.diff(idx) > 0)
+        assert np.array_equal(pk, P[idx].astype(np.float64) * 2.0 ** -40)
+        assert np.all((p[idx] == 1.0) == (pk == 1.0))
+
+
+def test_systematic_capped_blocks_always_taken_and_unbiased_total():
+    """Every p = 1 block is in every sample; the Horvitz-Thompson total of a
+    fixed vector, averaged over the U grid, equals its true total (each
+    block is counted P_j/2^28 times out of 4096, weighted by 2^40/P_j)."""
+    rng = np.random.default_rng(5)
+    s = rng.random(300) ** 6
+    s[[7, 100, 250]] = 40.0                          # three blocks certain to be capped
+    p = oracle.sip_probabilities((s / s.sum() * 0.999).astype(np.float32), 40)
+    assert (p == 1.0).sum() > 0
+    P = oracle.systematic_sizes(p)
+    x = rng.standard_normal(300)
+    grid = _u_grid()
+    est = 0.0
+    for U in grid:
+        sel = oracle.systematic_select(P, U)
+        assert sel[p == 1.0].all()
+        est += (x[sel] * (float(oracle.sip.SYS_UNIT) / P[sel].astype(np.float64))).sum()
+    est /= len(grid)
+    # each block's count is within one of its expectation: error <= sum |x_j| 2^40/(P_j 4096)
+    bound = (np.abs(x[P > 0]) * float(oracle.sip.SYS_UNIT) / (P[P > 0].astype(np.float64) * len(grid))).sum()
+    assert abs(est - x[P > 0].sum()) <= bound + 1e-9
+
+
+def test_systematic_uniform_range_and_row_dependence():
+    us = {oracle.systematic_uniform(99, b, h, r) for b in range(2) for h in range(3) for r in range(5)}
+    assert len(us) == 30 and all(0 <= u < oracle.sip.SYS_UNIT for u in us)
