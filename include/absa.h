@@ -71,13 +71,31 @@ typedef enum absa_dtype {
 
 typedef struct absa_plan_s* absa_plan;
 
+/* Sampling design of a plan (step 4). Both take each KV block with the same
+ * capped probability p and weight it by 1/p [hamidun, SIP paragraph]:
+ *   POISSON     one independent draw per block (Philox uniform u < p); the
+ *               count per query block is K only in expectation.
+ *   SYSTEMATIC  a fixed-size design for the pages' fixed budget per query
+ *               block: sizes P = floor(p 2^40), one Philox uniform U per
+ *               query block, and block j is taken iff a point U + k 2^40
+ *               falls in its cumulative interval [P_0+..+P_{j-1},
+ *               P_0+..+P_j). The count is K (K - 1 or K + 1 only where
+ *               rounding left the fixed-point total off K 2^40), each block
+ *               is taken with probability P 2^-40 exactly, and that is the
+ *               p the plan records and weights by. */
+typedef enum absa_sampling {
+    ABSA_SAMPLING_POISSON = 0,
+    ABSA_SAMPLING_SYSTEMATIC = 1
+} absa_sampling;
+
 /* Plan parameters. query_block must be 128 and kv_block 4 (the sizes the
  * pages give: [hamidun, IBCS paragraph] 128-query blocks, [hamidun, kernel
  * paragraph] KV blocks of at most 4 tokens). n_clusters in [1, 16]
  * (pages: 8); kmeans_iters in [1, 64] (pages: a fixed count, not stated;
  * default 4). budget_blocks = K, the KV blocks each query block samples in
  * expectation, in [1, N/4]. seed = the sampler's 64-bit Philox key; a plan
- * rebuilt at a later step takes a new seed. keep_intermediates != 0 keeps
+ * rebuilt at a later step takes a new seed. sampling = an absa_sampling
+ * value (default POISSON). keep_intermediates != 0 keeps
  * the mean keys, centroids, weights and scores on the device for
  * absa_plan_export_intermediate; otherwise they are freed when the plan is
  * built. */
@@ -89,7 +107,7 @@ typedef struct absa_plan_params {
     int64_t budget_blocks;
     uint64_t seed;
     int32_t keep_intermediates;
-    int32_t reserved;           /* must be 0 */
+    int32_t sampling;           /* absa_sampling */
 } absa_plan_params;
 
 /* Which retained intermediate absa_plan_export_intermediate copies. */
@@ -101,7 +119,8 @@ typedef enum absa_intermediate {
 } absa_intermediate;
 
 /* Fill *out with the defaults: 128, 4, 8 clusters, 4 iterations, budget 1,
- * seed 0, keep_intermediates 0. Returns ABSA_ERR_INVALID_ARG on NULL. */
+ * seed 0, keep_intermediates 0, POISSON sampling. Returns
+ * ABSA_ERR_INVALID_ARG on NULL. */
 absa_status absa_plan_params_init(absa_plan_params* out);
 
 /* Build a plan from Q and K: mean keys, IBCS k-means and scores, then SIP
@@ -117,12 +136,14 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype,
 /* Build a plan from caller-supplied IBCS scores (SIP only, step 4).
  * scores_dev: device float [B, H, QB, M]; every score must lie in [0, 1] and
  * every row must sum to less than 2, else ABSA_ERR_INVALID_ARG (checked on
- * the device, reported when the call returns). Given the same fp32 scores
- * and seed, the plan (row pointers, indices, p) is bit-identical to the
+ * the device, reported when the call returns). sampling: an absa_sampling
+ * value, else ABSA_ERR_INVALID_ARG. Given the same fp32 scores, seed and
+ * design, the plan (row pointers, indices, p) is bit-identical to the
  * documented fixed-point rule. Blocks like absa_plan_create. */
 absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
                                   int64_t N, int64_t d, int64_t budget_blocks,
-                                  uint64_t seed, void* hip_stream, absa_plan* out);
+                                  uint64_t seed, int32_t sampling, void* hip_stream,
+                                  absa_plan* out);
 
 /* Build a plan from a host CSR: rowptr int64 [rows+1] (rowptr[0] = 0,
  * non-decreasing), idx int32 [nnz] strictly ascending within each row and in

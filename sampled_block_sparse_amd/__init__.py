@@ -7,7 +7,7 @@ first call raises.
 
 The functions carry the C names:
   absa_plan_create(q, k, budget_blocks, seed, ...) -> Plan
-  absa_plan_from_scores(scores, N, d, budget_blocks, seed) -> Plan
+  absa_plan_from_scores(scores, N, d, budget_blocks, seed, sampling=...) -> Plan
   absa_plan_import(rowptr, idx, logw, p, B, H, N, d) -> Plan
   absa_sparse_attention(plan, q, k, v, out=None) -> out
   absa_dense_attention(q, k, v, out=None) -> out
@@ -28,6 +28,7 @@ __all__ = [
     "get_lib", "LIB_PATH", "ABSA_OK", "ABSA_ERR_INVALID_ARG", "ABSA_ERR_UNSUPPORTED",
     "ABSA_ERR_OUT_OF_MEMORY", "ABSA_ERR_DEVICE", "ABSA_ERR_PLAN_MISMATCH",
     "INTER_MEAN_KEYS", "INTER_CENTROIDS", "INTER_WEIGHTS", "INTER_SCORES",
+    "SAMPLING_POISSON", "SAMPLING_SYSTEMATIC",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libabsa.so")
@@ -43,7 +44,21 @@ _i64, _u64, _i32, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.
 class _Params(ctypes.Structure):
     _fields_ = [("query_block", _i32), ("kv_block", _i32), ("n_clusters", _i32),
                 ("kmeans_iters", _i32), ("budget_blocks", _i64), ("seed", _u64),
-                ("keep_intermediates", _i32), ("reserved", _i32)]
+                ("keep_intermediates", _i32), ("sampling", _i32)]
+
+
+# absa_sampling
+SAMPLING_POISSON = 0
+SAMPLING_SYSTEMATIC = 1
+_SAMPLING = {"poisson": SAMPLING_POISSON, "systematic": SAMPLING_SYSTEMATIC}
+
+
+def _sampling_code(sampling) -> int:
+    if isinstance(sampling, str):
+        if sampling not in _SAMPLING:
+            raise ValueError(f"sampling must be one of {sorted(_SAMPLING)}")
+        return _SAMPLING[sampling]
+    return int(sampling)
 
 
 class AbsaError(RuntimeError):
@@ -69,7 +84,7 @@ def get_lib():
         "absa_plan_params_init": (_i32, [ctypes.POINTER(_Params)]),
         "absa_plan_create": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i64,
                                     ctypes.POINTER(_Params), _vp, ctypes.POINTER(_vp)]),
-        "absa_plan_from_scores": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp,
+        "absa_plan_from_scores": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _u64, _i32, _vp,
                                          ctypes.POINTER(_vp)]),
         "absa_plan_import": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp,
                                     ctypes.POINTER(_vp)]),
@@ -208,7 +223,7 @@ class Plan:
 
 def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed: int,
                      n_clusters: int = 8, kmeans_iters: int = 4,
-                     keep_intermediates: bool = False, stream=None) -> Plan:
+                     keep_intermediates: bool = False, sampling="poisson", stream=None) -> Plan:
     B, H, N, d = _shape4(q)
     if tuple(k.shape) != (B, H, N, d) or k.dtype != q.dtype:
         raise ValueError("q and k must share shape and dtype")
@@ -220,6 +235,7 @@ def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed:
     prm.budget_blocks = budget_blocks
     prm.seed = seed & 0xFFFFFFFFFFFFFFFF
     prm.keep_intermediates = 1 if keep_intermediates else 0
+    prm.sampling = _sampling_code(sampling)
     out = _vp()
     _check(lib.absa_plan_create(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, N, d,
                                 ctypes.byref(prm), _stream(stream), ctypes.byref(out)))
@@ -227,7 +243,7 @@ def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed:
 
 
 def absa_plan_from_scores(scores: torch.Tensor, N: int, d: int, budget_blocks: int, seed: int,
-                          stream=None) -> Plan:
+                          sampling="poisson", stream=None) -> Plan:
     if scores.dtype != torch.float32 or scores.dim() != 4:
         raise ValueError("scores must be float32 [B, H, QB, M]")
     B, H = int(scores.shape[0]), int(scores.shape[1])
@@ -235,8 +251,8 @@ def absa_plan_from_scores(scores: torch.Tensor, N: int, d: int, budget_blocks: i
         raise ValueError("scores must be [B, H, ceil(N/128), N/4]")
     out = _vp()
     _check(get_lib().absa_plan_from_scores(_dev(scores, "scores"), B, H, N, d, budget_blocks,
-                                           seed & 0xFFFFFFFFFFFFFFFF, _stream(stream),
-                                           ctypes.byref(out)))
+                                           seed & 0xFFFFFFFFFFFFFFFF, _sampling_code(sampling),
+                                           _stream(stream), ctypes.byref(out)))
     return Plan(out.value)
 
 

@@ -275,6 +275,16 @@ absa_status check_dtype(absa_dtype dt) {
     return ABSA_OK;
 }
 
+absa_status check_sampling(int32_t sampling) {
+    static_assert(ABSA_SAMPLING_POISSON == kSamplingPoisson &&
+                  ABSA_SAMPLING_SYSTEMATIC == kSamplingSystematic, "sampling codes");
+    if (sampling != ABSA_SAMPLING_POISSON && sampling != ABSA_SAMPLING_SYSTEMATIC)
+        return fail(ABSA_ERR_INVALID_ARG,
+                    "sampling must be ABSA_SAMPLING_POISSON or ABSA_SAMPLING_SYSTEMATIC (got %d)",
+                    (int)sampling);
+    return ABSA_OK;
+}
+
 void fill_dims(absa_plan_s* p, int64_t B, int64_t H, int64_t N, int64_t d) {
     p->B = B; p->H = H; p->N = N; p->d = d;
     p->M = N / kKvBlock;
@@ -301,12 +311,12 @@ absa_status sip_temps(A& a, const absa_plan_s* P, PlanTemps& t) {
 // the score check flag, then the fill kernel. Returns with the fill queued;
 // the caller synchronises.
 absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_t seed,
-                    hipStream_t s, DeviceArena& arena, const PlanTemps& t) {
+                    int sampling, hipStream_t s, DeviceArena& arena, const PlanTemps& t) {
     const int64_t rows = P->rows;
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
     ABSA_HIP(hipMemsetAsync(t.status, 0, sizeof(PlanStatus), s), "clear plan status");
-    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, t.capmask,
-                              t.keepmask, t.rowinfo, t.counts, t.status, s),
+    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, sampling,
+                              t.capmask, t.keepmask, t.rowinfo, t.counts, t.status, s),
              "SIP count kernel");
     ABSA_HIP(launch_scan(t.counts, rows, P->rowptr, t.status, s), "row scan kernel");
     PlanStatus host{};
@@ -322,7 +332,7 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
     ABSA_TRY(arena.alloc(&P->p, P->nnz, "plan probabilities"));
     if (P->nnz > 0) {
         ABSA_HIP(launch_sip_fill(scores, rows, P->M, t.capmask, t.keepmask, t.rowinfo, P->rowptr,
-                                 P->idx, P->logw, P->p, s),
+                                 sampling, P->idx, P->logw, P->p, s),
                  "SIP fill kernel");
     }
     return ABSA_OK;
@@ -372,7 +382,7 @@ absa_status absa_plan_params_init(absa_plan_params* out) {
     out->budget_blocks = 1;
     out->seed = 0;
     out->keep_intermediates = 0;
-    out->reserved = 0;
+    out->sampling = ABSA_SAMPLING_POISSON;
     return ABSA_OK;
 }
 
@@ -394,7 +404,7 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     if (params->kmeans_iters < 1 || params->kmeans_iters > 64)
         return fail(ABSA_ERR_INVALID_ARG, "kmeans_iters must lie in [1, 64] (got %d)",
                     params->kmeans_iters);
-    if (params->reserved != 0) return fail(ABSA_ERR_INVALID_ARG, "params.reserved must be 0");
+    ABSA_TRY(check_sampling(params->sampling));
     const int64_t M = N / kKvBlock;
     if (params->budget_blocks < 1 || params->budget_blocks > M)
         return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
@@ -450,7 +460,8 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
         ABSA_HIP(launch_scores(t.cent, t.w, t.kq, t.kx, B * H, P->QB, M, static_cast<int>(d), C,
                                t.part, t.scores, s),
                  "score kernel");
-        ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, s, arena, t));
+        ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, params->sampling, s,
+                         arena, t));
         keep(arena, P);
         // the workspace is released (and may be reused) only once the build
         // has finished on the device
@@ -469,11 +480,12 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
 
 absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H, int64_t N,
                                   int64_t d, int64_t budget_blocks, uint64_t seed,
-                                  void* hip_stream, absa_plan* out) {
+                                  int32_t sampling, void* hip_stream, absa_plan* out) {
     if (!out) return fail(ABSA_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!scores_dev) return fail(ABSA_ERR_INVALID_ARG, "scores is NULL");
     ABSA_TRY(check_shape(B, H, N, d));
+    ABSA_TRY(check_sampling(sampling));
     const int64_t M = N / kKvBlock;
     if (budget_blocks < 1 || budget_blocks > M)
         return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
@@ -493,7 +505,7 @@ absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
         carve.cap = measure.used;
         ABSA_TRY(sip_temps(carve, P, t));
         DeviceArena arena(s);
-        ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, s, arena, t));
+        ABSA_TRY(run_sip(P, scores_dev, budget_blocks, seed, sampling, s, arena, t));
         keep(arena, P);
         ABSA_HIP(hipStreamSynchronize(s), "plan completion");
         return ABSA_OK;

@@ -13,6 +13,10 @@ constexpr int kMaxClusters = 16;
 
 enum Dtype : int { kBF16 = 0, kF32 = 1 };
 
+// Sampling designs of the plan (values of absa_plan_params.sampling).
+constexpr int kSamplingPoisson = 0;
+constexpr int kSamplingSystematic = 1;
+
 // Per-row outcome of the capped water-filling, written by the SIP count
 // kernel and read by the fill kernel.
 //   mode 0: every still-active block has p = 1
@@ -52,7 +56,8 @@ hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, co
                          float2* part, float* scores, hipStream_t s);
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
-                            int64_t M, int64_t budget, uint64_t seed, uint64_t* capmask,
+                            int64_t M, int64_t budget, uint64_t seed, int sampling,
+                            uint64_t* capmask,
                             uint64_t* keepmask, SipRow* rowinfo, int64_t* counts,
                             PlanStatus* status, hipStream_t s);
 
@@ -62,8 +67,8 @@ hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr,
 hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
                            const uint64_t* capmask, const uint64_t* keepmask,
                            const SipRow* rowinfo,
-                           const int64_t* rowptr, int32_t* idx, float* logw, double* p,
-                           hipStream_t s);
+                           const int64_t* rowptr, int sampling, int32_t* idx, float* logw,
+                           double* p, hipStream_t s);
 
 // fp32 -> bf16 (round to nearest even) of n elements, n a multiple of 8.
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);

@@ -792,6 +792,45 @@ __device__ __forceinline__ void sip_uniform_pair(uint64_t seed, int64_t b, int64
     u1 = static_cast<double>(((static_cast<uint64_t>(c[2]) << 32) | c[3]) >> 11) * 0x1.0p-53;
 }
 
+// Fixed-size design: the row's uniform U in [0, 2^40), from the Philox
+// counter (2^32 - 1, r, h, b) (block pairs never reach that index), words
+// (x0, x1) as (hi, lo).
+__device__ __forceinline__ uint64_t sys_uniform(uint64_t seed, int64_t b, int64_t h, int64_t r) {
+    uint32_t c[4] = {0xFFFFFFFFu, static_cast<uint32_t>(r), static_cast<uint32_t>(h),
+                     static_cast<uint32_t>(b)};
+    philox_10(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+    return ((static_cast<uint64_t>(c[0]) << 32) | c[1]) >> 24;
+}
+// P = floor(p 2^40) for p in [0, 1]: exact (a power-of-two scaling, then floor)
+__device__ __forceinline__ uint64_t sys_size(double p) {
+    return static_cast<uint64_t>(floor(p * 0x1.0p40));
+}
+// number of points U + k 2^40 (k >= 0) below x
+__device__ __forceinline__ uint64_t sys_points_below(uint64_t x, uint64_t U) {
+    return x > U ? ((x - U - 1) >> 40) + 1 : 0;
+}
+// 64-bit sum over the wave, the inclusive scan over its lanes, and the scan's
+// last value (the wave total), in fixed orders (integers: exact anyway)
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_last_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // floor(s * 2^52) of an fp32 score in [0, 1], as an exact fp64 integer. Sums
 // of such integers below 2^53 are exact in fp64 in any order, which is the
 // order-free fixed-point arithmetic the sampler's rule asks for.
@@ -872,11 +911,12 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 template <int NT, int MAXP>
 __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
-    uint64_t seed, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
+    uint64_t seed, int sampling, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     constexpr int kSipPairsPerPass = NT;                 // block pairs per pass
     __shared__ double redd[NT / 64];
     __shared__ int redi[NT / 64];
+    __shared__ uint64_t redu[NT / 64];
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
@@ -1038,13 +1078,8 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     int ibase_d = ibase, prem_d = prem;
     asm volatile("" : "+v"(ibase_d), "+s"(prem_d));
     auto in_row_d = [&](int k) { return kPassStep * k < prem_d; };
-    auto draw = [&](int k, float2 v) {
-        const int i = ibase_d + kPassStep * k;
-        double u0 = 1.0, u1 = 1.0;
-        sip_uniform_pair(seed, b, h, r, i, u0, u1);
-        const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
-        const bool keep0 = 2 * i < M32 && u0 < sip_p(cap0, ri, v.x);
-        const bool keep1 = 2 * i + 1 < M32 && u1 < sip_p(cap1, ri, v.y);
+    // The pass's keep and cap bits leave as mask words in block order.
+    auto emit = [&](int k, bool keep0, bool keep1, bool cap0, bool cap1) {
         // Bit b of word w0 is block 2 (i_0 + b/2) + (b & 1), held by lane b/2
         // (of word w0 + 1: lane 32 + b/2). Lane b fetches that lane's four
         // bits and the ballots give the words in block order.
@@ -1067,15 +1102,94 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
         }
         kept += (keep0 ? 1 : 0) + (keep1 ? 1 : 0);
     };
-    if constexpr (MAXP > 0) {
+    if (sampling == kSamplingPoisson) {
+        // one Bernoulli(p) per block
+        auto draw = [&](int k, float2 v) {
+            const int i = ibase_d + kPassStep * k;
+            double u0 = 1.0, u1 = 1.0;
+            sip_uniform_pair(seed, b, h, r, i, u0, u1);
+            const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
+            const bool keep0 = 2 * i < M32 && u0 < sip_p(cap0, ri, v.x);
+            const bool keep1 = 2 * i + 1 < M32 && u1 < sip_p(cap1, ri, v.y);
+            emit(k, keep0, keep1, cap0, cap1);
+        };
+        if constexpr (MAXP > 0) {
 #pragma unroll
-        for (int k = 0; k < MAXP; ++k) {
-            if (in_row_d(k)) draw(k, get_pair(k));
-            // one pair's Philox at a time: keeps the register count low
-            __builtin_amdgcn_sched_barrier(0);
+            for (int k = 0; k < MAXP; ++k) {
+                if (in_row_d(k)) draw(k, get_pair(k));
+                // one pair's Philox at a time: keeps the register count low
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            for (int k = 0; k < npass; ++k) draw(k, pair_at(k));
         }
     } else {
-        for (int k = 0; k < npass; ++k) draw(k, pair_at(k));
+        // Fixed-size design: sizes P_j = floor(p_j 2^40), exact integer
+        // prefix sums in block order, one uniform U per row; block j is
+        // taken iff a point U + k 2^40 falls in [C_{j-1}, C_j).
+        const uint64_t U = sys_uniform(seed, b, h, r);
+        struct PairSizes { uint64_t p0, p1; bool cap0, cap1; };
+        auto sizes = [&](int k, float2 v) {
+            const int i = ibase_d + kPassStep * k;
+            PairSizes z;
+            z.cap0 = v.x >= thr_min;
+            z.cap1 = v.y >= thr_min;
+            z.p0 = (2 * i < M32) ? sys_size(sip_p(z.cap0, ri, v.x)) : 0;
+            z.p1 = (2 * i + 1 < M32) ? sys_size(sip_p(z.cap1, ri, v.y)) : 0;
+            return z;
+        };
+        // pass k given the prefix before the pair of lane 0 (wave-uniform)
+        auto take = [&](int k, const PairSizes& z, uint64_t before, uint64_t incl) {
+            const uint64_t c_prev = before + incl - (z.p0 + z.p1);
+            const uint64_t c0 = c_prev + z.p0, c1 = c0 + z.p1;
+            const uint64_t n_prev = sys_points_below(c_prev, U), n0 = sys_points_below(c0, U);
+            emit(k, n0 > n_prev, sys_points_below(c1, U) > n0, z.cap0, z.cap1);
+        };
+        if constexpr (MAXP > 0) {
+            // the wave's range is contiguous: its prefix is the earlier
+            // waves' totals, then pass by pass within the wave
+            uint64_t wt = 0;
+#pragma unroll
+            for (int k = 0; k < MAXP; ++k) {
+                if (in_row_d(k)) {
+                    const PairSizes z = sizes(k, get_pair(k));
+                    wt += z.p0 + z.p1;
+                }
+            }
+            wt = wave_sum_u64(wt);
+            if (lane == 0) redu[wave] = wt;
+            __syncthreads();
+            uint64_t before = 0;
+            for (int w2 = 0; w2 < wave; ++w2) before += redu[w2];
+#pragma unroll
+            for (int k = 0; k < MAXP; ++k) {
+                if (in_row_d(k)) {
+                    const PairSizes z = sizes(k, get_pair(k));
+                    const uint64_t incl = wave_scan_u64(z.p0 + z.p1);
+                    take(k, z, before, incl);
+                    before += wave_last_u64(incl);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // pass k covers pairs NT k .. NT k + NT - 1 across the waves
+            uint64_t run = 0;
+            for (int k = 0; k < npass; ++k) {
+                const PairSizes z = sizes(k, pair_at(k));
+                const uint64_t incl = wave_scan_u64(z.p0 + z.p1);
+                if (lane == 63) redu[wave] = incl;
+                __syncthreads();
+                uint64_t before = run, tot = 0;
+                for (int w2 = 0; w2 < NT / 64; ++w2) {
+                    const uint64_t t = redu[w2];
+                    if (w2 < wave) before += t;
+                    tot += t;
+                }
+                take(k, z, before, incl);
+                run += tot;
+                __syncthreads();
+            }
+        }
     }
     const int tk = block_sum(kept, redi);
     if (tid == 0) {
@@ -1133,8 +1247,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int64_t* __restrict__ 
 __global__ __launch_bounds__(256) void sip_fill_kernel(
     const float* __restrict__ scores, int64_t M, const uint64_t* __restrict__ capmask,
     const uint64_t* __restrict__ keepmask, const SipRow* __restrict__ rowinfo,
-    const int64_t* __restrict__ rowptr, int32_t* __restrict__ idx, float* __restrict__ logw,
-    double* __restrict__ p_out) {
+    const int64_t* __restrict__ rowptr, int sampling, int32_t* __restrict__ idx,
+    float* __restrict__ logw, double* __restrict__ p_out) {
     __shared__ int wtot[4];
     __shared__ int word_pos[256];
     __shared__ int64_t q_at[4][64];                    // queued output positions, per wave
@@ -1147,15 +1261,20 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     const SipRow ri = rowinfo[row];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The plan's p: the design's inclusion probability (under the fixed-size
+    // design, p rounded down to a multiple of 2^-40).
+    auto incl_p = [&](double p) {
+        return (sampling == kSamplingSystematic) ? floor(p * 0x1.0p40) * 0x1.0p-40 : p;
+    };
     // p and -ln p of a block that is neither capped nor queued
-    const double p_direct = (ri.mode == 1) ? ri.c : 1.0;
+    const double p_direct = incl_p((ri.mode == 1) ? ri.c : 1.0);
     const float lw_direct = (p_direct == 1.0) ? 0.0f : static_cast<float>(-log(p_direct));
     int nq = 0;                                        // queue length (wave-uniform)
     auto flush = [&]() {
         if (lane < nq) {
             const int64_t at = q_at[wave][lane];
             const int j = q_j[wave][lane];
-            const double p = sip_p(false, ri, sg[j]);
+            const double p = incl_p(sip_p(false, ri, sg[j]));
             logw[at] = (p == 1.0) ? 0.0f : static_cast<float>(-log(p));
             p_out[at] = p;
         }
@@ -1329,7 +1448,8 @@ hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, co
 }
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB, int64_t M,
-                            int64_t budget, uint64_t seed, uint64_t* capmask, uint64_t* keepmask,
+                            int64_t budget, uint64_t seed, int sampling, uint64_t* capmask,
+                            uint64_t* keepmask,
                             SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
     // 512 threads per row, the scores of up to 32 pairs per thread in
@@ -1340,7 +1460,7 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
     return launch_checked([&] {
 #define ABSA_SIP_LAUNCH(NT, MP)                                                                  \
     hipLaunchKernelGGL((sip_count_kernel<NT, MP>), dim3(rows), dim3(NT), 0, s, scores, H, QB,   \
-                       M, budget, seed, capmask, keepmask, rowinfo, counts, status)
+                       M, budget, seed, sampling, capmask, keepmask, rowinfo, counts, status)
         if (npass <= 8) ABSA_SIP_LAUNCH(512, 8);
         else if (npass <= 16) ABSA_SIP_LAUNCH(512, 16);
         else if (npass <= 20) ABSA_SIP_LAUNCH(512, 20);
@@ -1360,10 +1480,10 @@ hipError_t launch_scan(const int64_t* counts, int64_t rows, int64_t* rowptr, Pla
 
 hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M, const uint64_t* capmask,
                            const uint64_t* keepmask, const SipRow* rowinfo, const int64_t* rowptr,
-                           int32_t* idx, float* logw, double* p, hipStream_t s) {
+                           int sampling, int32_t* idx, float* logw, double* p, hipStream_t s) {
     return launch_checked([&] {
         hipLaunchKernelGGL(sip_fill_kernel, dim3(rows), dim3(256), 0, s, scores, M, capmask,
-                           keepmask, rowinfo, rowptr, idx, logw, p);
+                           keepmask, rowinfo, rowptr, sampling, idx, logw, p);
     });
 }
 

@@ -103,7 +103,8 @@ def _create(**kw):
     (dict(n_clusters=0), absa.ABSA_ERR_UNSUPPORTED),
     (dict(n_clusters=17), absa.ABSA_ERR_UNSUPPORTED),
     (dict(kmeans_iters=0), absa.ABSA_ERR_INVALID_ARG),
-    (dict(reserved=1), absa.ABSA_ERR_INVALID_ARG),
+    (dict(sampling=2), absa.ABSA_ERR_INVALID_ARG),
+    (dict(sampling=-1), absa.ABSA_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects(kw, status):
     assert _create(**kw) == status
@@ -117,12 +118,14 @@ def test_other_calls_reject_before_device_work():
                                 ctypes.byref(out)) == absa.ABSA_ERR_INVALID_ARG
     assert lib.absa_plan_create(_FAKE, _FAKE, 0, 1, 1, 1024, 64, None, None,
                                 None) == absa.ABSA_ERR_INVALID_ARG
-    assert lib.absa_plan_from_scores(None, 1, 1, 1024, 64, 10, 0, None,
+    assert lib.absa_plan_from_scores(None, 1, 1, 1024, 64, 10, 0, 0, None,
                                      ctypes.byref(out)) == absa.ABSA_ERR_INVALID_ARG
-    assert lib.absa_plan_from_scores(_FAKE, 1, 1, 1024, 64, 0, 0, None,
+    assert lib.absa_plan_from_scores(_FAKE, 1, 1, 1024, 64, 0, 0, 0, None,
                                      ctypes.byref(out)) == absa.ABSA_ERR_INVALID_ARG
-    assert lib.absa_plan_from_scores(_FAKE, 1, 1, 1000, 80, 10, 0, None,
+    assert lib.absa_plan_from_scores(_FAKE, 1, 1, 1000, 80, 10, 0, 0, None,
                                      ctypes.byref(out)) == absa.ABSA_ERR_UNSUPPORTED
+    assert lib.absa_plan_from_scores(_FAKE, 1, 1, 1024, 64, 10, 0, 5, None,
+                                     ctypes.byref(out)) == absa.ABSA_ERR_INVALID_ARG
     assert lib.absa_sparse_attention(None, _FAKE, _FAKE, _FAKE, _FAKE, 0, 1, 1, 1024, 64,
                                      None) == absa.ABSA_ERR_INVALID_ARG
     assert lib.absa_dense_attention(_FAKE, _FAKE, None, _FAKE, 0, 1, 1, 1024, 64,

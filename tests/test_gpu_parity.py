@@ -71,15 +71,20 @@ def test_dense_vs_oracle(case):
         check_output(to64(out), oracle.dense_attention(c["Q"], c["K"], c["V"]), "dense")
 
 
-def test_plan_from_oracle_scores_is_bit_exact(case):
+@pytest.mark.parametrize("sampling", ["poisson", "systematic"])
+def test_plan_from_oracle_scores_is_bit_exact(case, sampling):
     c = case
     seed = synth.sip_seed(0)
     s32 = c["scores"].astype(np.float32)
     plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), c["N"], c["d"], c["budget"],
-                                      seed)
-    ref = oracle.plan_from_scores(s32, c["B"], c["H"], c["N"], c["d"], c["budget"], seed)
-    n1 = check_plan_exact(plan.export(), ref, c["name"])
+                                      seed, sampling=sampling)
+    ref = oracle.plan_from_scores(s32, c["B"], c["H"], c["N"], c["d"], c["budget"], seed,
+                                  sampling)
+    n1 = check_plan_exact(plan.export(), ref, f"{c['name']} {sampling}")
     print(f"logw entries 1 ulp apart: {n1} of {ref.idx.size}")
+    if sampling == "systematic":
+        counts = np.diff(ref.rowptr)
+        assert np.all(np.abs(counts - c["budget"]) <= 1), (counts.min(), counts.max())
 
 
 def test_sparse_with_imported_oracle_plan(case):
@@ -129,6 +134,29 @@ def test_plan_create_stages_and_output(case):
     torch.cuda.synchronize()
     ref = oracle.plan_attention(c["Q"], c["K"], c["V"], oracle_plan_of(gp, B, H, N, d))
     check_output(to64(out), ref, "sparse (own plan)")
+
+
+def test_plan_create_systematic_end_to_end():
+    """absa_plan_create with the fixed-size design: the plan is the oracle's
+    systematic draw on the GPU's own scores (bit-exact), every row takes the
+    budget (+-1), and the output matches the oracle's HT attention given it."""
+    q, k, v = _inputs(B=1, H=2, N=3000, d=128, seed=21)
+    B, H, N, d = q.shape
+    M, QB = N // 4, (N + 127) // 128
+    budget = synth.budget_blocks(10, M)
+    seed = synth.sip_seed(6)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    plan = absa.absa_plan_create(qd, kd, budget, seed, keep_intermediates=True,
+                                 sampling="systematic")
+    s = plan.export_intermediate(absa.INTER_SCORES).reshape(B, H, QB, M)
+    gp = plan.export()
+    ref_plan = oracle.plan_from_scores(s, B, H, N, d, budget, seed, "systematic")
+    check_plan_exact(gp, ref_plan, "plan_create systematic")
+    assert np.all(np.abs(np.diff(gp["rowptr"]) - budget) <= 1)
+    out = absa.absa_sparse_attention(plan, qd, kd, vd)
+    torch.cuda.synchronize()
+    ref = oracle.plan_attention(to64(q), to64(k), to64(v), oracle_plan_of(gp, B, H, N, d))
+    check_output(to64(out), ref, "sparse (systematic plan)")
 
 
 def test_full_budget_equals_dense():
@@ -296,15 +324,17 @@ def _sip_edge_rows(M=256, K=16):
     return np.stack(rows)[None, None]                                 # [1, 1, QB=8, M]
 
 
+@pytest.mark.parametrize("sampling", ["poisson", "systematic"])
 @pytest.mark.parametrize("K", [1, 16, 100, 255, 256])
-def test_sip_rounding_edges_bit_exact(K):
+def test_sip_rounding_edges_bit_exact(K, sampling):
     s32 = _sip_edge_rows()
     assert s32.shape == (1, 1, 8, 256)
     N, d = 1024, 64
     seed = 0x5EED0042
-    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, K, seed)
-    ref = oracle.plan_from_scores(s32, 1, 1, N, d, K, seed)
-    check_plan_exact(plan.export(), ref, f"edge rows K={K}")
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, K, seed,
+                                      sampling=sampling)
+    ref = oracle.plan_from_scores(s32, 1, 1, N, d, K, seed, sampling)
+    check_plan_exact(plan.export(), ref, f"edge rows K={K} {sampling}")
 
 
 def test_fill_queue_many_uncapped_blocks():
@@ -327,8 +357,9 @@ def test_fill_queue_many_uncapped_blocks():
     check_plan_exact(gp, ref, "many uncapped")
 
 
+@pytest.mark.parametrize("sampling", ["poisson", "systematic"])
 @pytest.mark.parametrize("M", [9001, 23000, 32765, 40002])
-def test_sip_row_length_tiers(M):
+def test_sip_row_length_tiers(M, sampling):
     """The SIP count kernel keeps a row's scores in registers in tiers of
     8, 16, 20, 24 or 32 block pairs per thread and re-reads them from memory
     for longer rows; each wave owns one contiguous range of pairs, the last
@@ -350,13 +381,16 @@ def test_sip_row_length_tiers(M):
     s32 = (s / s.sum(axis=-1, keepdims=True) * 0.999).astype(np.float32)[None, None]
     budget = M // 10
     seed = synth.sip_seed(5)
-    print(f"[sip tiers] M={M} rows={QB}", flush=True)
-    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, budget, seed)
+    print(f"[sip tiers] M={M} rows={QB} {sampling}", flush=True)
+    plan = absa.absa_plan_from_scores(torch.from_numpy(s32).to(DEV), N, d, budget, seed,
+                                      sampling=sampling)
     gp = plan.export()
     plan.destroy()
+    if sampling == "systematic":
+        assert np.all(np.abs(np.diff(gp["rowptr"]) - budget) <= 1)
     for r in sorted({0, 1, 2, 3, QB // 2, QB // 2 + 1, QB - 2, QB - 1}):
         p = oracle.sip_probabilities(s32[0, 0, r], budget)
-        idx, logw, pk = oracle.sip_draw_row(p, seed, 0, 0, r)
+        idx, logw, pk = oracle.draw_row(p, seed, 0, 0, r, sampling)
         lo, hi = gp["rowptr"][r], gp["rowptr"][r + 1]
         np.testing.assert_array_equal(gp["idx"][lo:hi], idx, err_msg=f"M={M} row {r}")
         assert np.array_equal(gp["p"][lo:hi].view(np.uint64), pk.view(np.uint64)), f"M={M} row {r}"
