@@ -50,6 +50,12 @@ def parse():
                     help="target length of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--sampling", default="poisson", choices=["poisson", "systematic"],
+                    help="sampling design of the plan (default poisson)")
+    ap.add_argument("--sampling-study", action="store_true",
+                    help="design comparison instead of the benchmark line: small video-shaped "
+                         "layer, budgets 5/10/20%%, 8 seeds each, Poisson against systematic "
+                         "sampling: output error against dense, blocks per row, plan time")
     ap.add_argument("--reuse-sweep", action="store_true",
                     help="plan-reuse report instead of the benchmark line: small video-shaped "
                          "layer, plan built at step 0, attention at steps 0-3 on drifting "
@@ -192,10 +198,62 @@ def reuse_sweep():
                       "drift": "Q/K/V += 0.05 N(0,1) per step", "rows": rows}))
 
 
+def sampling_study(seeds=8):
+    """Poisson against fixed-size (systematic) sampling on the small
+    video-shaped layer: for each budget and design, the sparse output's error
+    against dense attention over several seeds (mean and spread), the spread
+    of blocks per row, and the plan time; prints one JSON object."""
+    import torch
+    import sampled_block_sparse_amd as absa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x.to(dev) for x in synth.make_inputs("small"))
+    B, H, N, d = (int(x) for x in q.shape)
+    M = N // 4
+    dense = absa.absa_dense_attention(q, k, v)
+    df = dense.float()
+    dn = float(torch.linalg.vector_norm(df))
+    out = torch.empty_like(q)
+    rows = []
+    for pct in (5, 10, 20):
+        budget = synth.budget_blocks(pct, M)
+        for design in ("poisson", "systematic"):
+            errs, maxabs, cmin, cmax, cstd, plan_ms = [], [], [], [], [], []
+            for s in range(seeds):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                plan = absa.absa_plan_create(q, k, budget, synth.sip_seed(s), sampling=design)
+                plan_ms.append((time.perf_counter() - t0) * 1e3)
+                absa.absa_sparse_attention(plan, q, k, v, out)
+                torch.cuda.synchronize()
+                diff = out.float() - df
+                errs.append(float(torch.linalg.vector_norm(diff)) / dn)
+                maxabs.append(float(diff.abs().max()))
+                c = np.diff(plan.export()["rowptr"])
+                cmin.append(int(c.min()))
+                cmax.append(int(c.max()))
+                cstd.append(float(c.std()))
+                plan.destroy()
+            rows.append({
+                "budget_pct": pct, "budget_blocks": budget, "sampling": design, "seeds": seeds,
+                "rel_l2_vs_dense_mean": float(np.mean(errs)),
+                "rel_l2_vs_dense_std": float(np.std(errs)),
+                "max_abs_vs_dense_mean": float(np.mean(maxabs)),
+                "blocks_per_row_min": min(cmin), "blocks_per_row_max": max(cmax),
+                "blocks_per_row_std_mean": float(np.mean(cstd)),
+                "plan_ms_median": float(np.median(plan_ms[1:] if seeds > 1 else plan_ms)),
+            })
+    print(json.dumps({"mode": "sampling_study", "workload": WORKLOADS["small"], "rows": rows}))
+
+
 def main():
     args = parse()
     if args.reuse_sweep:
         reuse_sweep()
+        return
+    if args.sampling_study:
+        sampling_study()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -231,7 +289,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        plan = absa.absa_plan_create(qd, kd, budget, seed)
+        plan = absa.absa_plan_create(qd, kd, budget, seed, sampling=args.sampling)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -328,7 +386,7 @@ def main():
         "config": {"workload": WORKLOADS[name] if pct == cfg["budget_pct"]
                    else WORKLOADS[name].rsplit(",", 1)[0] + f", budget {pct}%",
                    "B": B, "H": H, "N": N, "d": d, "budget_blocks": budget,
-                   "parallelism": "single GPU"},
+                   "sampling": args.sampling, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sparse_attn_ms": round(attn_ms, 4),
@@ -343,6 +401,8 @@ def main():
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_vs_dense": round(dense_ms / attn_ms, 3) if dense_ms else None,
         "keep_fraction": round(keep_fraction, 5),
+        "blocks_per_row": {"min": int(counts.min()), "max": int(counts.max()),
+                           "mean": round(float(counts.mean()), 2)},
         "rel_l2_vs_dense": round(rel_l2_vs_dense, 5) if rel_l2_vs_dense is not None else None,
         "value_definition": "dense-equivalent flop 4*B*H*N^2*d per step / (plan + sparse attention) time",
     }
