@@ -56,6 +56,10 @@ def parse():
                     help="design comparison instead of the benchmark line: small video-shaped "
                          "layer, budgets 5/10/20%%, 8 seeds each, Poisson against systematic "
                          "sampling: output error against dense, blocks per row, plan time")
+    ap.add_argument("--selection-study", action="store_true",
+                    help="what each selection rule retains at equal budget on the small "
+                         "video-shaped layer: exact top-K, IBCS (C=8) and mean-query (C=1) "
+                         "scores with top-K or SIP, 128-token blocks; attention mass and error")
     ap.add_argument("--reuse-sweep", action="store_true",
                     help="plan-reuse report instead of the benchmark line: small video-shaped "
                          "layer, plan built at step 0, attention at steps 0-3 on drifting "
@@ -247,8 +251,92 @@ def sampling_study(seeds=8):
     print(json.dumps({"mode": "sampling_study", "workload": WORKLOADS["small"], "rows": rows}))
 
 
+def _topk_plan(score, K):
+    """CSR of the K best blocks of every row (ascending indices, p = 1)."""
+    rows, M = score.shape
+    idx = np.sort(np.argpartition(-score, K - 1, axis=1)[:, :K], axis=1).astype(np.int32)
+    rowptr = np.arange(rows + 1, dtype=np.int64) * K
+    return rowptr, idx.reshape(-1), np.zeros(rows * K, np.float32), np.ones(rows * K)
+
+
+def selection_study(heads=2):
+    """What the plan's choices retain, at equal budget, on the small
+    video-shaped layer (first `heads` heads): per selection rule, the mean
+    true attention mass of the chosen blocks (exact block masses from fp64
+    softmax rows on the CPU) and the error of the sparse output against
+    dense attention (the GPU kernel run on each rule's plan). Rules: exact
+    top-K by true mass (the bound), top-K by IBCS score (C = 8) and by the
+    single mean-query score (C = 1), SIP sampling on each of those two
+    scores, and top-K/32 128-token blocks by their summed IBCS score (the
+    coarse granularity the pages contrast with 4-token blocks). Prints one
+    JSON object."""
+    import torch
+    import sampled_block_sparse_amd as absa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x[:, :heads].contiguous() for x in synth.make_inputs("small"))
+    B, H, N, d = (int(x) for x in q.shape)
+    M, QB = N // 4, (N + 127) // 128
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    dense = absa.absa_dense_attention(qd, kd, vd).float()
+    dn = float(torch.linalg.vector_norm(dense))
+    # exact mass of every (row, KV block): mean over the row's queries of the
+    # softmax probability summed over the block's 4 keys
+    mass = np.zeros((B * H * QB, M))
+    Q64, K64 = q.double().numpy(), k.double().numpy()
+    for b in range(B):
+        for h in range(H):
+            for r in range(QB):
+                z = Q64[b, h, 128 * r:128 * r + 128] @ K64[b, h].T / np.sqrt(d)
+                z = np.exp(z - z.max(axis=1, keepdims=True))
+                z /= z.sum(axis=1, keepdims=True)
+                mass[(b * H + h) * QB + r] = z.reshape(z.shape[0], M, 4).sum(axis=2).mean(axis=0)
+
+    def run(plan, name, budget):
+        gp = plan.export()
+        out = absa.absa_sparse_attention(plan, qd, kd, vd).float()
+        torch.cuda.synchronize()
+        rows_ = np.repeat(np.arange(B * H * QB), np.diff(gp["rowptr"]))
+        kept = np.zeros(B * H * QB)
+        np.add.at(kept, rows_, mass[rows_, gp["idx"]])
+        diff = out - dense
+        return {"rule": name, "budget_blocks": budget,
+                "retained_mass_mean": float(kept.mean()), "retained_mass_min": float(kept.min()),
+                "rel_l2_vs_dense": float(torch.linalg.vector_norm(diff)) / dn,
+                "max_abs_vs_dense": float(diff.abs().max())}
+
+    res = []
+    for pct in (5, 10, 20):
+        K = synth.budget_blocks(pct, M)
+        seed = synth.sip_seed(0)
+        scores = {}
+        for C in (8, 1):
+            plan = absa.absa_plan_create(qd, kd, K, seed, n_clusters=C, keep_intermediates=True)
+            scores[C] = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M).astype(np.float64)
+            res.append(run(plan, f"C={C} scores + SIP", K))
+            plan.destroy()
+        for name, sc in (("exact top-K", mass), ("C=8 top-K", scores[8]), ("C=1 top-K", scores[1])):
+            res.append(run(absa.absa_plan_import(*_topk_plan(sc, K), B, H, N, d), name, K))
+        # 128-token blocks: 32 consecutive KV blocks each, K/32 of them per row
+        Kc = max(1, K // 32)
+        coarse = scores[8].reshape(-1, M // 32, 32).sum(axis=2)
+        rp, ic, _, _ = _topk_plan(coarse, Kc)
+        idx = (ic.reshape(-1, Kc)[:, :, None] * 32 + np.arange(32)).reshape(-1).astype(np.int32)
+        rows = B * H * QB
+        plan = absa.absa_plan_import(np.arange(rows + 1, dtype=np.int64) * Kc * 32, idx,
+                                     np.zeros(idx.size, np.float32), np.ones(idx.size), B, H, N, d)
+        res.append(run(plan, "128-token blocks, C=8 top", Kc * 32))
+    print(json.dumps({"mode": "selection_study",
+                      "workload": WORKLOADS["small"].replace("H=8", f"H={H} (first heads)"),
+                      "rows": res}))
+
+
 def main():
     args = parse()
+    if args.selection_study:
+        selection_study()
+        return
     if args.reuse_sweep:
         reuse_sweep()
         return
