@@ -56,6 +56,10 @@ def parse():
                     help="design comparison instead of the benchmark line: small video-shaped "
                          "layer, budgets 5/10/20%%, 8 seeds each, Poisson against systematic "
                          "sampling: output error against dense, blocks per row, plan time")
+    ap.add_argument("--schedule", action="store_true",
+                    help="the pages' 50-step schedule on one layer of --workload: dense for "
+                         "the first 10 steps, then sparse with the plan rebuilt every 4 steps; "
+                         "total attention time against dense at every step")
     ap.add_argument("--selection-study", action="store_true",
                     help="what each selection rule retains at equal budget on the small "
                          "video-shaped layer: exact top-K, IBCS (C=8) and mean-query (C=1) "
@@ -332,8 +336,72 @@ def selection_study(heads=2):
                       "rows": res}))
 
 
+def schedule_run(workload, steps=50, dense_first=10, every=4):
+    """The pages' denoising schedule on one attention layer [hamidun, kernel
+    paragraph and "how it was measured"]: the first `dense_first` of `steps`
+    steps run full attention, then each step runs the sparse kernel on a
+    plan rebuilt every `every` steps. Times every piece (HIP events for the
+    kernels, wall time for the plan, which synchronises once) on the same
+    Q/K/V each step (a timing run; the reuse sweep measures drift), and
+    compares with full attention at every step. Prints one JSON object."""
+    import torch
+    import sampled_block_sparse_amd as absa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[workload]
+    qd, kd, vd = (x.to(dev) for x in synth.make_inputs(workload))
+    B, H, N, d = (int(x) for x in qd.shape)
+    budget = synth.budget_blocks(cfg["budget_pct"], N // 4)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    absa.absa_dense_attention(qd, kd, vd, out)            # warm-up of both paths
+    absa.absa_sparse_attention(absa.absa_plan_create(qd, kd, budget, 1), qd, kd, vd, out)
+    torch.cuda.synchronize()
+    dense_ms, plan_ms, sparse_ms = [], [], []
+    plan = None
+    t_start = time.perf_counter()
+    for s in range(steps):
+        if s < dense_first:
+            dense_ms.append(timed(lambda: absa.absa_dense_attention(qd, kd, vd, out)))
+            continue
+        if (s - dense_first) % every == 0:
+            t0 = time.perf_counter()
+            plan = absa.absa_plan_create(qd, kd, budget, synth.sip_seed(s))
+            torch.cuda.synchronize()
+            plan_ms.append((time.perf_counter() - t0) * 1e3)
+        sparse_ms.append(timed(lambda: absa.absa_sparse_attention(plan, qd, kd, vd, out)))
+    wall_ms = (time.perf_counter() - t_start) * 1e3
+    total = sum(dense_ms) + sum(plan_ms) + sum(sparse_ms)
+    all_dense = steps * float(np.mean(dense_ms))
+    print(json.dumps({
+        "mode": "schedule", "workload": WORKLOADS[workload], "steps": steps,
+        "dense_first": dense_first, "plan_every": every, "plans": len(plan_ms),
+        "dense_ms_mean": round(float(np.mean(dense_ms)), 3),
+        "plan_ms_mean": round(float(np.mean(plan_ms)), 3),
+        "sparse_ms_mean": round(float(np.mean(sparse_ms)), 3),
+        "attention_ms_total": round(total, 1),
+        "attention_ms_total_all_dense": round(all_dense, 1),
+        "speedup_vs_all_dense": round(all_dense / total, 3),
+        "wall_ms_total": round(wall_ms, 1),
+        "note": "all-dense total = steps x the mean measured dense step",
+    }))
+
+
 def main():
     args = parse()
+    if args.schedule:
+        schedule_run(args.workload)
+        return
     if args.selection_study:
         selection_study()
         return
