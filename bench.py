@@ -66,8 +66,11 @@ def parse():
                          "scores with top-K or SIP, 128-token blocks; attention mass and error")
     ap.add_argument("--reuse-sweep", action="store_true",
                     help="plan-reuse report instead of the benchmark line: small video-shaped "
-                         "layer, plan built at step 0, attention at steps 0-3 on drifting "
-                         "Q/K/V, budgets 5/10/20%%; time and error against dense per step")
+                         "layer (or --workload with --reuse-wan for the Wan2.1-like one), plan "
+                         "built at step 0, attention at steps 0-3 on drifting Q/K/V, budgets "
+                         "5/10/20%%; time and error against dense per step")
+    ap.add_argument("--reuse-wan", action="store_true",
+                    help="with --reuse-sweep: run it on the Wan2.1-like layer")
     return ap.parse_args()
 
 
@@ -148,18 +151,18 @@ def cpu_baseline(q, k, v, budget, seed, seconds):
     return layer_s, done, elapsed, threads
 
 
-def reuse_sweep():
+def reuse_sweep(workload="small"):
     """[hamidun, kernel paragraph]: a plan is rebuilt every 4 denoising steps
-    and reused in between. Builds the plan at step 0 on the small
-    video-shaped layer and runs the sparse and the dense kernel at steps 0-3,
-    Q/K/V drifting by 0.05 N(0,1) per step; prints one JSON object."""
+    and reused in between. Builds the plan at step 0 on a video-shaped layer
+    and runs the sparse and the dense kernel at steps 0-3, Q/K/V drifting by
+    0.05 N(0,1) per step; prints one JSON object."""
     import torch
     import sampled_block_sparse_amd as absa
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q0, k0, v0 = synth.make_inputs("small")
-    B, H, N, d = (int(x) for x in q0.shape)
+    x0 = synth.make_inputs(workload)
+    B, H, N, d = (int(x) for x in x0[0].shape)
     M = N // 4
     stream = torch.cuda.current_stream()
 
@@ -176,83 +179,45 @@ def reuse_sweep():
             ms.append(e0.elapsed_time(e1))
         return float(np.median(ms))
 
+    # the drifting inputs of steps 0..3 (the same for every budget), on the device
+    steps = []
+    cur = x0
+    for step in range(synth.REUSE_STEPS):
+        if step:
+            cur = tuple(synth.drift(x, seed=100 * step + i) for i, x in enumerate(cur))
+        steps.append(tuple(x.to(dev) for x in cur))
+        print(f"[reuse] inputs of step {step} ready", file=sys.stderr, flush=True)
+    del cur, x0
+    dense_out = []
+    for qd, kd, vd in steps:
+        dense_out.append(absa.absa_dense_attention(qd, kd, vd))
+    dense_ms = [timed(lambda: absa.absa_dense_attention(qd, kd, vd, dense_out[i]))
+                for i, (qd, kd, vd) in enumerate(steps)]
+
     rows = []
     for pct in (5, 10, 20):
         budget = synth.budget_blocks(pct, M)
-        q, k, v = q0, k0, v0
-        qd, kd = q.to(dev), k.to(dev)
+        qd, kd, _ = steps[0]
+        absa.absa_plan_create(qd, kd, budget, synth.sip_seed(0)).destroy()   # warm-up
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         plan = absa.absa_plan_create(qd, kd, budget, synth.sip_seed(0))
         plan_ms = (time.perf_counter() - t0) * 1e3
-        for step in range(synth.REUSE_STEPS):
-            if step:
-                q, k, v = (synth.drift(x, seed=100 * step + i) for i, x in enumerate((q, k, v)))
-            qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        for step, (qd, kd, vd) in enumerate(steps):
             out = torch.empty_like(qd)
-            dense = torch.empty_like(qd)
             sparse_ms = timed(lambda: absa.absa_sparse_attention(plan, qd, kd, vd, out))
-            dense_ms = timed(lambda: absa.absa_dense_attention(qd, kd, vd, dense))
-            diff = (out.float() - dense.float())
+            diff = (out.float() - dense_out[step].float())
             rows.append({
                 "budget_pct": pct, "budget_blocks": budget, "step": step,
                 "plan_built_at_step": 0, "plan_ms": round(plan_ms, 3) if step == 0 else None,
-                "sparse_attn_ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
-                "rel_l2_vs_dense": float(diff.norm() / dense.float().norm()),
+                "sparse_attn_ms": round(sparse_ms, 4), "dense_ms": round(dense_ms[step], 4),
+                "rel_l2_vs_dense": float(diff.norm() / dense_out[step].float().norm()),
                 "max_abs_vs_dense": float(diff.abs().max()),
             })
+            del diff
         plan.destroy()
-    print(json.dumps({"mode": "reuse_sweep", "workload": WORKLOADS["small"],
+    print(json.dumps({"mode": "reuse_sweep", "workload": WORKLOADS[workload],
                       "drift": "Q/K/V += 0.05 N(0,1) per step", "rows": rows}))
-
-
-def sampling_study(seeds=8):
-    """Poisson against fixed-size (systematic) sampling on the small
-    video-shaped layer: for each budget and design, the sparse output's error
-    against dense attention over several seeds (mean and spread), the spread
-    of blocks per row, and the plan time; prints one JSON object."""
-    import torch
-    import sampled_block_sparse_amd as absa
-    import synth
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    q, k, v = (x.to(dev) for x in synth.make_inputs("small"))
-    B, H, N, d = (int(x) for x in q.shape)
-    M = N // 4
-    dense = absa.absa_dense_attention(q, k, v)
-    df = dense.float()
-    dn = float(torch.linalg.vector_norm(df))
-    out = torch.empty_like(q)
-    rows = []
-    for pct in (5, 10, 20):
-        budget = synth.budget_blocks(pct, M)
-        for design in ("poisson", "systematic"):
-            errs, maxabs, cmin, cmax, cstd, plan_ms = [], [], [], [], [], []
-            for s in range(seeds):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                plan = absa.absa_plan_create(q, k, budget, synth.sip_seed(s), sampling=design)
-                plan_ms.append((time.perf_counter() - t0) * 1e3)
-                absa.absa_sparse_attention(plan, q, k, v, out)
-                torch.cuda.synchronize()
-                diff = out.float() - df
-                errs.append(float(torch.linalg.vector_norm(diff)) / dn)
-                maxabs.append(float(diff.abs().max()))
-                c = np.diff(plan.export()["rowptr"])
-                cmin.append(int(c.min()))
-                cmax.append(int(c.max()))
-                cstd.append(float(c.std()))
-                plan.destroy()
-            rows.append({
-                "budget_pct": pct, "budget_blocks": budget, "sampling": design, "seeds": seeds,
-                "rel_l2_vs_dense_mean": float(np.mean(errs)),
-                "rel_l2_vs_dense_std": float(np.std(errs)),
-                "max_abs_vs_dense_mean": float(np.mean(maxabs)),
-                "blocks_per_row_min": min(cmin), "blocks_per_row_max": max(cmax),
-                "blocks_per_row_std_mean": float(np.mean(cstd)),
-                "plan_ms_median": float(np.median(plan_ms[1:] if seeds > 1 else plan_ms)),
-            })
-    print(json.dumps({"mode": "sampling_study", "workload": WORKLOADS["small"], "rows": rows}))
 
 
 def _topk_plan(score, K):
@@ -406,7 +371,7 @@ def main():
         selection_study()
         return
     if args.reuse_sweep:
-        reuse_sweep()
+        reuse_sweep(args.workload if args.workload != "wan" or args.reuse_wan else "small")
         return
     if args.sampling_study:
         sampling_study()
