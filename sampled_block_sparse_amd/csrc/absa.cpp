@@ -63,6 +63,12 @@ absa_status hip_fail(hipError_t e, const char* what) {
     } while (0)
 #define ABSA_HIP_RET(call, what) ABSA_HIP(call, what)
 
+#define ABSA_TRY(expr)                       \
+    do {                                     \
+        absa_status s_ = (expr);             \
+        if (s_ != ABSA_OK) return s_;        \
+    } while (0)
+
 // Allocation failure can be forced for tests: ABSA_FAULT_INJECT=alloc.
 bool inject_alloc_failure() {
     const char* v = std::getenv("ABSA_FAULT_INJECT");
@@ -192,6 +198,65 @@ Workspace* device_workspace(int dev) {
     return g_ws[dev].get();
 }
 
+// A second stream per device for plan-build work that does not depend on the
+// caller stream's next kernel: the mean keys run there beside the k-means
+// (one streams K from HBM, the other computes in fp64 on Q). Created on first
+// use with the default priority and flags that keep it from synchronising
+// with the null stream; kept until the process ends. Builds on one device
+// share it; each build orders its work with events of its own.
+std::mutex g_side_mutex;
+std::vector<hipStream_t> g_side;
+
+absa_status device_side_stream(hipStream_t* out) {
+    int dev = 0;
+    ABSA_HIP_RET(hipGetDevice(&dev), "current device");
+    std::lock_guard<std::mutex> lock(g_side_mutex);
+    if (static_cast<size_t>(dev) >= g_side.size()) g_side.resize(dev + 1, nullptr);
+    if (!g_side[dev]) {
+        hipStream_t st = nullptr;
+        ABSA_HIP_RET(hipStreamCreateWithFlags(&st, hipStreamNonBlocking), "side stream");
+        g_side[dev] = st;
+    }
+    *out = g_side[dev];
+    return ABSA_OK;
+}
+
+// Work forked from stream `main` onto the device's side stream and joined
+// back: fork() makes the side stream wait for everything queued on main so
+// far; join() makes main wait for everything queued on the side stream since.
+// If the build fails between the two, the destructor waits for the side
+// stream, so nothing it runs outlives the build's buffers.
+class SideFork {
+  public:
+    explicit SideFork(hipStream_t main) : main_(main) {}
+    ~SideFork() {
+        if (side_ && !joined_) (void)hipStreamSynchronize(side_);
+        if (fork_) (void)hipEventDestroy(fork_);
+        if (join_) (void)hipEventDestroy(join_);
+    }
+    absa_status fork(hipStream_t* side) {
+        ABSA_TRY(device_side_stream(&side_));
+        ABSA_HIP_RET(hipEventCreateWithFlags(&fork_, hipEventDisableTiming), "fork event");
+        ABSA_HIP_RET(hipEventCreateWithFlags(&join_, hipEventDisableTiming), "join event");
+        ABSA_HIP_RET(hipEventRecord(fork_, main_), "fork record");
+        ABSA_HIP_RET(hipStreamWaitEvent(side_, fork_, 0), "fork wait");
+        *side = side_;
+        return ABSA_OK;
+    }
+    absa_status join() {
+        ABSA_HIP_RET(hipEventRecord(join_, side_), "join record");
+        ABSA_HIP_RET(hipStreamWaitEvent(main_, join_, 0), "join wait");
+        joined_ = true;
+        return ABSA_OK;
+    }
+
+  private:
+    hipStream_t main_;
+    hipStream_t side_ = nullptr;
+    hipEvent_t fork_ = nullptr, join_ = nullptr;
+    bool joined_ = false;
+};
+
 // A build's hold on a workspace block of at least `bytes` bytes.
 class WorkspaceLease {
   public:
@@ -246,12 +311,6 @@ struct PlanTemps {
     int64_t* counts = nullptr;
     PlanStatus* status = nullptr;
 };
-
-#define ABSA_TRY(expr)                       \
-    do {                                     \
-        absa_status s_ = (expr);             \
-        if (s_ != ABSA_OK) return s_;        \
-    } while (0)
 
 absa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
     if (B < 1 || H < 1) return fail(ABSA_ERR_INVALID_ARG, "B and H must be >= 1 (got %lld, %lld)",
@@ -452,11 +511,16 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
             ABSA_TRY(arena.alloc(&P->scores, P->rows * M, "scores"));
             t.kbar = P->kbar; t.cent = P->cent; t.w = P->w; t.scores = P->scores;
         }
-        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kq, t.kx, s),
+        // the mean keys (side stream) beside the k-means (caller stream)
+        SideFork fork(s);
+        hipStream_t side = nullptr;
+        ABSA_TRY(fork.fork(&side));
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kq, t.kx, side),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
                                t.cent, t.w, s),
                  "k-means kernel");
+        ABSA_TRY(fork.join());
         ABSA_HIP(launch_scores(t.cent, t.w, t.kq, t.kx, B * H, P->QB, M, static_cast<int>(d), C,
                                t.part, t.scores, s),
                  "score kernel");
