@@ -345,7 +345,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     // (scale > 0). alpha is 1 exactly when the running max did not grow, and
     // 0 on the first tile (m_run = -inf; a first tile always holds a valid
     // block, so its max is finite).
-    constexpr int kSmItems = 8 + 1 + 32 + 16;
     // The running max and the row sum are kept as 4 partials each (items
     // rotate over them) so that their updates form short dependency chains.
     // The row sum adds the bf16-rounded weights (one v_dot2 per packed pair

@@ -905,9 +905,10 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // its cap mask (s_j >= thr_min) to capmask, so the fill kernel reads the
 // score only of kept blocks that are not capped.
 // ---------------------------------------------------------------------------
-// NT threads per row (256 or 512): with fewer threads the per-round work
-// that every wave repeats (the threshold, the block reduction, its barriers)
-// is shared by fewer waves, at the cost of more scores held per thread.
+// NT threads per row (the launcher uses 512): with fewer threads the
+// per-round work that every wave repeats (the threshold, the block
+// reduction, its barriers) is shared by fewer waves, at the cost of more
+// scores held per thread.
 template <int NT, int MAXP>
 __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
