@@ -452,12 +452,36 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     // operand reads (one slot of 32 consecutive keys) hit distinct banks; a
     // stored slot's key and logical slot follow from its position. Keys past
     // M repeat key M-1 (their logits are never used).
-    // 32-bit index arithmetic (M < 2^19), recomputed per tile: the opaque
-    // copy of the lane index keeps the compiler from hoisting the per-lane
-    // offsets of every load out of the loop (they would not fit in registers).
+    // A lane's offset within a tile does not depend on the tile, so a tile
+    // whose 64 keys all lie below M adds its start to the loads' scalar base
+    // (scalar arithmetic) and reuses the lane offsets computed once here.
+    // The last tile of a ragged row clamps its keys per lane instead, with
+    // 32-bit index arithmetic (M < 2^19) recomputed there; the opaque copy of
+    // the lane index keeps the compiler from hoisting that path's per-lane
+    // offsets out of the loop.
     const int M32 = static_cast<int>(M);
+    uint32_t goff[SLOTS / 256];
+    {
+        const int lk = lane / SPR, cs = lane % SPR;
+#pragma unroll
+        for (int i = 0; i < SLOTS / 256; ++i) {
+            const int sw = i * 256 + wave * 64;
+            const int k = (sw / SPR) % TK + lk;
+            goff[i] = static_cast<uint32_t>(k * (3 * D) + (sw / (TK * SPR)) * D +
+                                            (cs ^ score_swizzle<D>(k)) * 16);
+            asm volatile("" : "+v"(goff[i]));
+        }
+    }
     auto dma_tile = [&](int buf, int64_t u) __attribute__((always_inline)) {
         const int j0 = static_cast<int>((t0 + 2 * u) * kScoreTile);
+        if (j0 + TK <= M32) {
+            const int8_t* tb = kb + static_cast<int64_t>(j0) * (3 * D);
+#pragma unroll
+            for (int i = 0; i < SLOTS / 256; ++i)
+                lds_load16(tb, goff[i], &ks[buf][(i * 256 + wave * 64) * 16]);
+            if (wave == 0) lds_load4(kxb + j0, static_cast<uint32_t>(lane * 4), &kxs[buf][0]);
+            return;
+        }
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lk = ln / SPR, cs = ln % SPR;    // key offset and stored slot of the lane
