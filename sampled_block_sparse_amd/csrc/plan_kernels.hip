@@ -570,7 +570,8 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
     // key factor, post(g, ...) finishes subtile g after its phase, and
     // first(...) runs on subtile 0 alone before the loop.
     intx16 xa22, xa21, xa20, xb22, xb21, xb20;
-    auto pipeline = [&](auto&& item, auto&& pre, auto&& post, auto&& first) __attribute__((always_inline)) {
+    auto pipeline = [&](auto&& item, auto&& pre, auto&& post, auto&& first,
+                        auto&& after_barrier) __attribute__((always_inline)) {
         auto none = [](int) {};
         dma_tile(0, 0);
         lds_load_wait();
@@ -592,6 +593,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             const float cf1 = key_factor(buf, kScoreTile + col);
             lds_load_wait();
             __syncthreads();
+            after_barrier();
             if (2 * u + 1 < nsub) {
                 pre();
                 phase(buf ^ 1, 0, xa22, xa21, xa20,
@@ -670,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 #pragma unroll
             for (int i = 0; i < 16; ++i) zs[i] += __builtin_amdgcn_exp2f(dv[i]);
         };
-        pipeline(item, pre, post, first);
+        pipeline(item, pre, post, first, [] {});
         // The reference is uniform over each half: the sums add across its
         // 32 lanes (xor over lane bits 0..4). Chunk statistic of a row:
         // (R + kSlack, sum), i.e. the chunk's sum of 2^x is sum * 2^(R + kSlack).
@@ -719,29 +721,77 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 #pragma unroll
             for (int g = 0; g < RPW; ++g) pr[g] = 0.0f;
         };
+        // The scores of a subtile are written after the next barrier when the
+        // subtile is the first of its LDS tile: written at once, their stores
+        // would sit behind the tile loads issued earlier in the iteration and
+        // the barrier's wait for those loads would wait for them too. (Not
+        // with 16 or 32 rows per wave, C <= 2: the held values would spill.)
+        constexpr bool kDefer = RPW <= 8;
+        float held[kDefer ? RPW : 1];
+        int64_t held_g = -1;
+        auto store = [&](int64_t g, const float (&vals)[RPW]) __attribute__((always_inline)) {
+            const int jt = static_cast<int>((t0 + g) * kScoreTile);        // < M < 2^19
+            const bool ok = jt + col < M32;
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) {
+                // rows q whose slots lie in this lane's half
+                const int half_of_q = (CP >= 8) ? (q & 1) : (((q * CP) >> 2) & 1);
+                const int64_t rr = r0 + q;
+                if (half_of_q == half && rr < QB && ok) {
+                    // a wave-uniform row pointer: the lane adds only its column
+                    float* rowp = scores + (bh * QB + rr) * M + jt;
+                    rowp[col] = vals[q];
+                }
+            }
+        };
         auto post = [&](int64_t g, const intx16&, const intx16&, const intx16&,
                         float) __attribute__((always_inline)) {
-            const int64_t j = (t0 + g) * kScoreTile + col;
-            if (CP >= 8) {
-                // A query block's clusters span both halves: add the partner's.
-#pragma unroll
-                for (int q = 0; q < RPW; ++q) pr[q] += __shfl_xor(pr[q], 32);
-#pragma unroll
-                for (int q = 0; q < RPW; ++q) {
-                    const int64_t rr = r0 + q;
-                    if ((q & 1) == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[q];
-                }
-            } else {
+            if constexpr (!kDefer) {
+                // 16 or 32 rows per wave: written at once, 64-bit addresses per
+                // lane (wave-uniform row pointers for every row would stay live
+                // across the loop and spill)
+                const int64_t j = (t0 + g) * kScoreTile + col;
 #pragma unroll
                 for (int q = 0; q < RPW; ++q) {
-                    // rows q whose slots lie in this lane's half
                     const int half_of_q = ((q * CP) >> 2) & 1;
                     const int64_t rr = r0 + q;
                     if (half_of_q == half && rr < QB && j < M) scores[(bh * QB + rr) * M + j] = pr[q];
                 }
+                return;
+            }
+            float vals[RPW];
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) {
+                // CP >= 8: a query block's clusters span both halves: add the
+                // partner's (one lane exchange)
+                if (CP >= 8) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(pr[q]),
+                                                                    __float_as_int(pr[q]), false, false);
+                    vals[q] = __int_as_float(r[0]) + __int_as_float(r[1]);
+                } else {
+                    vals[q] = pr[q];
+                }
+            }
+            if constexpr (kDefer) {
+                if ((g & 1) == 0) {
+#pragma unroll
+                    for (int q = 0; q < RPW; ++q) held[q] = vals[q];
+                    held_g = g;
+                    return;
+                }
+            }
+            store(g, vals);
+        };
+        auto after_barrier = [&]() __attribute__((always_inline)) {
+            if constexpr (kDefer) {
+                if (held_g >= 0) {
+                    store(held_g, held);
+                    held_g = -1;
+                }
             }
         };
-        pipeline(item, pre, post, [](const intx16&, const intx16&, const intx16&, float) {});
+        pipeline(item, pre, post, [](const intx16&, const intx16&, const intx16&, float) {},
+                 after_barrier);
     }
 }
 
