@@ -1040,11 +1040,17 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
         vmax = fmaxf(vmax, v);
     };
     if constexpr (MAXP > 0) {
+        // every load first (the scores stay in these registers anyway), so
+        // their latencies overlap; then the sums
 #pragma unroll
         for (int k = 0; k < MAXP; ++k) {
             const int i = ibase + kPassStep * k;
-            const float2 v = in_row(k) ? load_pair(i) : make_float2(-1.0f, -1.0f);
-            set_pair(k, v);
+            set_pair(k, in_row(k) ? load_pair(i) : make_float2(-1.0f, -1.0f));
+        }
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int i = ibase + kPassStep * k;
+            const float2 v = get_pair(k);
             add_score(v.x, 2 * i);
             add_score(v.y, 2 * i + 1);
             __builtin_amdgcn_sched_barrier(0);
