@@ -899,11 +899,12 @@ __device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
     }
     return v;
 }
-__device__ __forceinline__ uint64_t wave_last_u64(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
+__device__ __forceinline__ uint64_t wave_last_u64(uint64_t v) { return readlane_u64(v, 63); }
 
 // floor(s * 2^52) of an fp32 score in [0, 1], as an exact fp64 integer. Sums
 // of such integers below 2^53 are exact in fp64 in any order, which is the
@@ -1364,7 +1365,11 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
     int64_t pos = rowptr[row];
     for (int base = 0; base < words; base += 256) {
         const int w = base + tid;
-        const int pc = (w < words) ? __popcll(km[w]) : 0;
+        // thread t holds word t of the chunk; the expansion below takes the
+        // words of its wave from their lanes (no dependent reloads)
+        const uint64_t kw_own = (w < words) ? km[w] : 0ull;
+        const uint64_t cw_own = (w < words) ? cm[w] : 0ull;
+        const int pc = __popcll(kw_own);
         int incl = pc;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1383,9 +1388,9 @@ __global__ __launch_bounds__(256) void sip_fill_kernel(
         const int wend = min(64, words - base - 64 * wave);
         for (int u = 0; u < wend; ++u) {
             const int wl = 64 * wave + u;                 // word within the chunk
-            const uint64_t kw = km[base + wl];            // wave-uniform
+            const uint64_t kw = readlane_u64(kw_own, u);  // word wl, wave-uniform
             if (kw == 0) continue;
-            const uint64_t cw = cm[base + wl];
+            const uint64_t cw = readlane_u64(cw_own, u);
             const uint64_t qw = (ri.mode == 2) ? (kw & ~cw) : 0ull;   // blocks to queue
             const int nqw = __popcll(qw);
             if (nq + nqw > 64) flush();
