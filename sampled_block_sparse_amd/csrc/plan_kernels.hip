@@ -166,16 +166,29 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
     // 16-byte global loads, stored as four 4-byte words (the padded LDS rows
     // are 4-byte aligned; a row of D values is a whole number of 16 bytes)
     {
+        // (all of a thread's loads are issued before its stores, so their
+        // latencies overlap; 256 threads, a fixed trip count)
         constexpr int V = 16 / static_cast<int>(sizeof(T));    // values per 16 bytes
+        constexpr int PER = kQueryBlock * (D / V) / 256;        // loads per thread
+        static_assert(kQueryBlock * (D / V) % 256 == 0, "whole loads per thread");
         const uint4* src = reinterpret_cast<const uint4*>(qrow);
-        for (int e = tid; e < n * (D / V); e += blockDim.x) {
-            const int i = e / (D / V), c = (e - i * (D / V)) * V;
-            const uint4 u = src[e];
-            uint32_t* dst = reinterpret_cast<uint32_t*>(qs + i * QS + c);
-            dst[0] = u.x;
-            dst[1] = u.y;
-            dst[2] = u.z;
-            dst[3] = u.w;
+        uint4 u[PER];
+#pragma unroll
+        for (int r2 = 0; r2 < PER; ++r2) {
+            const int e = tid + 256 * r2;
+            u[r2] = (e < n * (D / V)) ? src[e] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r2 = 0; r2 < PER; ++r2) {
+            const int e = tid + 256 * r2;
+            if (e < n * (D / V)) {
+                const int i = e / (D / V), c = (e - i * (D / V)) * V;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(qs + i * QS + c);
+                dst[0] = u[r2].x;
+                dst[1] = u[r2].y;
+                dst[2] = u[r2].z;
+                dst[3] = u[r2].w;
+            }
         }
     }
     __syncthreads();
