@@ -629,7 +629,6 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         // their new maxima, a wave-uniform branch.
         constexpr float kSlack = 16.0f;
         float nref[16], zs[16], dv[16];
-        bool over = false;
         // Re-basing of row i on the logits x of a subtile (x = -inf past M):
         // R = max(R, the half's largest x), the sum rescaled to the new R.
         auto rebase = [&](int i, float x) __attribute__((always_inline)) {
@@ -659,12 +658,11 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
                         float cf, int k) __attribute__((always_inline)) {
             dv[k] = fmaf(combine(i22, i21, i20, k), cf, nref[k]);
-            over = over || dv[k] > 0.0f;
             // pinned here, between the MFMAs: the compiler would otherwise
             // sink the whole computation past them, next to its use
             asm volatile("" : "+v"(dv[k]));
         };
-        auto pre = [&]() __attribute__((always_inline)) { over = false; };
+        auto pre = [&]() __attribute__((always_inline)) {};
         // Subtiles g >= 1 (the references are finite, so x = dv - nref): a
         // rare re-basing rewrites dv in place, then every subtile adds its
         // exponentials.
@@ -673,6 +671,12 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             if (g == 0) return;
             const int64_t t = t0 + g;
             const bool last_ragged = ragged && (t + 1) * kScoreTile > M;
+            // some dv > 0: the largest bit pattern read as a signed integer is
+            // positive (integer maxima: no NaN quieting of the operands)
+            int mb = __float_as_int(dv[0]);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mb = max(mb, __float_as_int(dv[i]));
+            const bool over = mb > 0;
             if (last_ragged || __builtin_amdgcn_ballot_w64(over) != 0) {
                 const bool ok = t * kScoreTile + col < M;
 #pragma unroll
