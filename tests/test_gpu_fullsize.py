@@ -33,6 +33,11 @@ def layer(request):
     dense = absa.absa_dense_attention(qd, kd, vd)
     torch.cuda.synchronize()
     gp = plan.export()
+    # the same layer under the fixed-size design (the plan build is
+    # deterministic, so its scores are the ones exported below)
+    splan = absa.absa_plan_create(qd, kd, budget, seed, sampling="systematic")
+    gp_sys = splan.export()
+    splan.destroy()
     rows = [0, QB - 1, 3 * QB + QB // 2, (H - 1) * QB + QB - 1, (H // 2) * QB + 7,
             (H - 1) * QB + 1]
     scores = {r: plan.export_intermediate(absa.INTER_SCORES, r * M, M) for r in rows}
@@ -46,7 +51,8 @@ def layer(request):
     plan.destroy()
     torch.cuda.empty_cache()
     return dict(name=name, q=q, k=k, v=v, B=B, H=H, N=N, d=d, M=M, QB=QB, budget=budget,
-                seed=seed, gp=gp, rows=rows, scores=scores, o_rows=o_rows, d_rows=d_rows)
+                seed=seed, gp=gp, gp_sys=gp_sys, rows=rows, scores=scores, o_rows=o_rows,
+                d_rows=d_rows)
 
 
 def _head(L, h):
@@ -105,3 +111,21 @@ def test_whole_plan_properties(layer):
     # Poisson sampling: the mean count per row is the budget
     z = (counts.mean() - L["budget"]) / (np.sqrt(L["budget"] / rows))
     assert abs(z) < 6, f"mean count {counts.mean():.2f} vs budget {L['budget']}"
+
+
+def test_systematic_plan_full_size(layer):
+    """The fixed-size design at full size: every row takes the budget (+-1)
+    and the sampled rows are the oracle's systematic draws on the GPU's
+    scores, bit for bit."""
+    L = layer
+    gp = L["gp_sys"]
+    counts = np.diff(gp["rowptr"])
+    assert np.all(np.abs(counts - L["budget"]) <= 1), (counts.min(), counts.max())
+    for row in L["rows"]:
+        h, r = divmod(row, L["QB"])
+        p = oracle.sip_probabilities(L["scores"][row], L["budget"])
+        idx, logw, pk = oracle.systematic_draw_row(p, L["seed"], 0, h, r)
+        lo, hi = gp["rowptr"][row], gp["rowptr"][row + 1]
+        np.testing.assert_array_equal(gp["idx"][lo:hi], idx)
+        assert np.array_equal(gp["p"][lo:hi].view(np.uint64), pk.view(np.uint64))
+        assert (ulp_diff_f32(gp["logw"][lo:hi], logw) <= 1).all()
