@@ -815,10 +815,33 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // Block-wide reductions.
 // ---------------------------------------------------------------------------
+// Wave sums with DPP row operations: within each 16-lane row by two quad
+// permutes and the half-row and row mirrors, then the two row broadcasts
+// (rows 1 and 3 take lane 15 of the row before, rows 2 and 3 lane 31);
+// lane 63 ends with the total, read into a scalar. (The sums taken here are
+// of integers, or of doubles that are multiples of 2^-52 below 2: exact in
+// any order.)
+template <int CTRL, int ROWS> __device__ __forceinline__ int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS> __device__ __forceinline__ double dpp_move(double v) {
+    const int lo = dpp_move<CTRL, ROWS>(__double2loint(v));
+    const int hi = dpp_move<CTRL, ROWS>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ double lane63(double v) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
 template <typename V> __device__ __forceinline__ V wave_sum(V v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v += dpp_move<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v += dpp_move<0x141, 0xf>(v);    // row_half_mirror
+    v += dpp_move<0x140, 0xf>(v);    // row_mirror
+    v += dpp_move<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return lane63(v);
 }
 
 template <typename V> __device__ V block_sum(V v, V* red) {
@@ -832,12 +855,14 @@ template <typename V> __device__ V block_sum(V v, V* red) {
     return t;
 }
 
-// An int and a double summed over the block with one pair of barriers.
+// An int and a double summed over the block with one barrier: the caller
+// alternates between two sets of slots (redi/redd and redi + 16/redd + 16),
+// so a slot is written again only after a later barrier that every wave
+// reaches after reading it.
 __device__ void block_sum2(int a, double b, int* redi, double* redd, int& ta, double& tb) {
     a = wave_sum(a);
     b = wave_sum(b);
     const int wave = threadIdx.x >> 6;
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) {
         redi[wave] = a;
         redd[wave] = b;
@@ -1007,8 +1032,9 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     uint64_t seed, int sampling, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     constexpr int kSipPairsPerPass = NT;                 // block pairs per pass
-    __shared__ double redd[NT / 64];
-    __shared__ int redi[NT / 64];
+    static_assert(NT / 64 <= 16, "reduction slots");
+    __shared__ double redd[32];        // [16, 32): rounds 0, 2, ...; [0, 16): block_sum, rounds 1, 3, ...
+    __shared__ int redi[32];
     __shared__ uint64_t redu[NT / 64];
     const int64_t row = blockIdx.x;
     const float* sg = scores + row * M;
@@ -1098,6 +1124,7 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
     double S = total;
     float thr_min = INFINITY;
     SipRow ri;
+    int round = 0;
     for (;;) {
         const int64_t left = budget - taken;
         if (left >= n_active) { ri.mode = 0; ri.c = 1.0; break; }
@@ -1141,7 +1168,11 @@ __global__ __launch_bounds__(NT, 4) void sip_count_kernel(
         // integers below 2^53, exact in any order)
         int tcap;
         double tsum;
-        block_sum2(ncap, scap.value(), redi, redd, tcap, tsum);
+        // the first round takes the second slot set: block_sum's slots may
+        // still be read by waves that have not yet left it
+        const int slot = (round & 1) ? 0 : 16;
+        ++round;
+        block_sum2(ncap, scap.value(), redi + slot, redd + slot, tcap, tsum);
         if (tcap == 0) { ri.mode = 2; ri.c = c; break; }
         taken += tcap;
         n_active -= tcap;
