@@ -100,6 +100,43 @@ __global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
     if (d0 == 0) kx[blk] = ex;
 }
 
+// Wave sums with DPP row operations: within each 16-lane row by two quad
+// permutes and the half-row and row mirrors, then the two row broadcasts
+// (rows 1 and 3 take lane 15 of the row before, rows 2 and 3 lane 31);
+// lane 63 ends with the total, read into a scalar. (The sums taken here are
+// of integers, or of doubles that are multiples of 2^-52 below 2: exact in
+// any order.)
+template <int CTRL, int ROWS> __device__ __forceinline__ int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS> __device__ __forceinline__ double dpp_move(double v) {
+    const int lo = dpp_move<CTRL, ROWS>(__double2loint(v));
+    const int hi = dpp_move<CTRL, ROWS>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ double lane63(double v) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+// Sum over each 16-lane row, in every lane of the row.
+template <typename V> __device__ __forceinline__ V row_sum16(V v) {
+    v += dpp_move<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v += dpp_move<0x141, 0xf>(v);    // row_half_mirror
+    v += dpp_move<0x140, 0xf>(v);    // row_mirror
+    return v;
+}
+template <typename V> __device__ __forceinline__ V wave_sum(V v) {
+    v += dpp_move<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v += dpp_move<0x141, 0xf>(v);    // row_half_mirror
+    v += dpp_move<0x140, 0xf>(v);    // row_mirror
+    v += dpp_move<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return lane63(v);
+}
+
 // ---------------------------------------------------------------------------
 // IBCS k-means [hamidun, IBCS paragraph; edumints, IBCS item]: one workgroup
 // per query block. Lloyd iterations in fp64 on the block's queries in their
@@ -206,8 +243,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T* __restrict__ q, in
             const int m = tid >> 4, sub = tid & 15;
             double a = 0.0;
             for (int dd = sub; dd < D; dd += 16) a = fma(ct[dd][m], ct[dd][m], a);
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+            a = row_sum16(a);             // the 16 lanes of slot m form one DPP row
             if (sub == 0) cc[m] = a;
         }
         // q_i . c_m over channel half hd, for every cluster slot.
@@ -815,35 +851,6 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // Block-wide reductions.
 // ---------------------------------------------------------------------------
-// Wave sums with DPP row operations: within each 16-lane row by two quad
-// permutes and the half-row and row mirrors, then the two row broadcasts
-// (rows 1 and 3 take lane 15 of the row before, rows 2 and 3 lane 31);
-// lane 63 ends with the total, read into a scalar. (The sums taken here are
-// of integers, or of doubles that are multiples of 2^-52 below 2: exact in
-// any order.)
-template <int CTRL, int ROWS> __device__ __forceinline__ int dpp_move(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
-}
-template <int CTRL, int ROWS> __device__ __forceinline__ double dpp_move(double v) {
-    const int lo = dpp_move<CTRL, ROWS>(__double2loint(v));
-    const int hi = dpp_move<CTRL, ROWS>(__double2hiint(v));
-    return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
-__device__ __forceinline__ double lane63(double v) {
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
-                            __builtin_amdgcn_readlane(__double2loint(v), 63));
-}
-template <typename V> __device__ __forceinline__ V wave_sum(V v) {
-    v += dpp_move<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
-    v += dpp_move<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
-    v += dpp_move<0x141, 0xf>(v);    // row_half_mirror
-    v += dpp_move<0x140, 0xf>(v);    // row_mirror
-    v += dpp_move<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
-    v += dpp_move<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
-    return lane63(v);
-}
-
 template <typename V> __device__ V block_sum(V v, V* red) {
     v = wave_sum(v);
     const int wave = threadIdx.x >> 6;
