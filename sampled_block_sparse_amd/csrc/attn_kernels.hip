@@ -432,6 +432,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
             // tile that is stale K and the result is never used), one MFMA
             // per chunk with its K operand read two chunks ahead, and the
             // softmax items of tile t spread over the chunks.
+            // A wave runs its QK^T phase at raised priority, so that while
+            // it streams these MFMAs the other wave of the SIMD, in its VALU
+            // heavy P V phase, fills the issue slots in between (measured:
+            // about 1.3% faster; raising it over the P V phase instead gained
+            // nothing).
+            __builtin_amdgcn_s_setprio(1);
             SmState st;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -470,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
                     sm_item(item_a(ia), Scur, st, pw);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
             // Keep the packed weights of keys 0..31 computed here, inside the
             // interleaved phase: without this the compiler sinks them past
             // the rescale branch below, next to their use.
