@@ -6,7 +6,12 @@ A step is one pass of the whole hot path over the layer's Q/K/V, which are
 resident in HBM before timing starts: the plan (mean keys, IBCS k-means and
 scores, SIP probabilities, draws and CSR) followed by the gathered sparse
 attention. The dense flash-attention comparator is timed separately. Rank 0
-prints one JSON line. See the design doc for the definitions of every figure.
+prints one JSON line: `value` is the dense-equivalent flop of the layer
+(4 B H N^2 d) over the step time; `roofline` rates the sparse attention
+kernel (useful flop per launch over its HIP-event time, against the bf16
+MFMA peak; `traffic` is the HBM bytes of one launch from the FETCH_SIZE and
+WRITE_SIZE counters, valid for the attention source they were taken on);
+`cpu_baseline` times the fp64 oracle on a sample of plan rows.
 """
 from __future__ import annotations
 
@@ -378,7 +383,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path shards by head with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     import sampled_block_sparse_amd as absa
