@@ -767,8 +767,16 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
         float pr[RPW];
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
                         float cf, int k) __attribute__((always_inline)) {
-            pr[slot_of(k) / CP] +=
-                __builtin_amdgcn_exp2f(fmaf(combine(i22, i21, i20, k), cf, bias[k]));
+            const float e = __builtin_amdgcn_exp2f(fmaf(combine(i22, i21, i20, k), cf, bias[k]));
+            if constexpr (CP == 2) {
+                // row (k/4)*4 + 2*half + (k%4)/2: both candidates updated with
+                // compile-time indices (indexing by the lane's half spills)
+                const int q0 = (k >> 2) * 4 + ((k & 3) >> 1);
+                pr[q0] += half ? 0.0f : e;
+                pr[q0 + 2] += half ? e : 0.0f;
+            } else {
+                pr[slot_of(k) / CP] += e;
+            }
         };
         auto pre = [&]() __attribute__((always_inline)) {
 #pragma unroll

@@ -173,7 +173,7 @@ def test_full_budget_equals_dense():
     check_output(to64(sparse), oracle.dense_attention(to64(q), to64(k), to64(v)), "budget 100%")
 
 
-@pytest.mark.parametrize("C,T", [(1, 4), (4, 2), (16, 4), (8, 1)])
+@pytest.mark.parametrize("C,T", [(1, 4), (2, 3), (4, 2), (16, 4), (8, 1)])
 def test_cluster_and_iteration_variants(C, T):
     q, k, v = _inputs(B=1, H=2, N=1000, d=64, seed=11)
     Q, K = to64(q), to64(k)
