@@ -1040,9 +1040,14 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // NT threads per row (the launcher uses 512): with fewer threads the
 // per-round work that every wave repeats (the threshold, the block
 // reduction, its barriers) is shared by fewer waves, at the cost of more
-// scores held per thread.
+// scores held per thread. Up to 20 pairs per thread the kernel is built for
+// three workgroups per CU (6 waves per SIMD, at most 80 VGPRs): at 20 pairs
+// this spills 40 bytes per lane, but the third workgroup hides more of the
+// latency of the rounds' reductions than the spill costs (2.42 against
+// 2.65 ms on 40 x 591 rows of 18,900 blocks); at 24 and 32 pairs the scores
+// alone fill most of the 80 registers, and those tiers keep two workgroups.
 template <int NT, int MAXP>
-__global__ __launch_bounds__(NT, 4) void sip_count_kernel(
+__global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
     uint64_t seed, int sampling, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
