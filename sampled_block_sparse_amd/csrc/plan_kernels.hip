@@ -1157,17 +1157,26 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
         const float thr = fp32_at_least(cap_threshold(c) * 0x1.0p-52);
         int ncap = 0;
         FixedSum scap;
+        // If this round caps anything, thr < thr_min and thr becomes the new
+        // thr_min, so the largest score below thr (m) is the next vmax; if
+        // it caps nothing the rounds end and vmax is not read again.
+        float m = -1.0f;
         auto test = [&](float v) {
             // opaque copy: keeps the conversions of every block from being
             // hoisted out of the rounds loop (64 live doubles otherwise)
             asm volatile("" : "+v"(v));
-            if (v >= thr && v < thr_min) {
-                ++ncap;
-                scap.add(v);
+            if (v >= thr) {
+                if (v < thr_min) {
+                    ++ncap;
+                    scap.add(v);
+                }
+            } else {
+                m = fmaxf(m, v);
             }
         };
+        // a wave none of whose uncapped scores reaches thr has no new cap,
+        // and its vmax stays the largest score below the next thr_min
         if constexpr (MAXP > 0) {
-            // a wave none of whose uncapped scores reaches thr has no new cap
             if (__builtin_amdgcn_ballot_w64(vmax >= thr) != 0) {
 #pragma unroll
                 for (int k = 0; k < MAXP; ++k) {
@@ -1176,6 +1185,7 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
                     test(v.y);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                vmax = m;
             }
         } else {
             for (int k = 0; k < npass; ++k) {
@@ -1198,21 +1208,6 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
         n_active -= tcap;
         S -= tsum;
         thr_min = fminf(thr_min, thr);
-        if constexpr (MAXP > 0) {
-            // this thread's largest score below the new thr_min
-            if (__builtin_amdgcn_ballot_w64(vmax >= thr_min) != 0) {
-                float m = -1.0f;
-#pragma unroll
-                for (int k = 0; k < MAXP; ++k) {
-                    const float2 v = get_pair(k);
-                    float x = v.x, y = v.y;
-                    asm volatile("" : "+v"(x), "+v"(y));
-                    m = x < thr_min ? fmaxf(m, x) : m;
-                    m = y < thr_min ? fmaxf(m, y) : m;
-                }
-                vmax = m;
-            }
-        }
     }
     ri.thr = thr_min;
 
