@@ -1037,15 +1037,15 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // its cap mask (s_j >= thr_min) to capmask, so the fill kernel reads the
 // score only of kept blocks that are not capped.
 // ---------------------------------------------------------------------------
-// NT threads per row (the launcher uses 512): with fewer threads the
+// NT threads per row (the launcher uses 512 or 768): with fewer threads the
 // per-round work that every wave repeats (the threshold, the block
 // reduction, its barriers) is shared by fewer waves, at the cost of more
 // scores held per thread. Up to 20 pairs per thread the kernel is built for
 // three workgroups per CU (6 waves per SIMD, at most 80 VGPRs): at 20 pairs
 // this spills 40 bytes per lane, but the third workgroup hides more of the
 // latency of the rounds' reductions than the spill costs (2.42 against
-// 2.65 ms on 40 x 591 rows of 18,900 blocks); at 24 and 32 pairs the scores
-// alone fill most of the 80 registers, and those tiers keep two workgroups.
+// 2.65 ms on 40 x 591 rows of 18,900 blocks); at 32 pairs the scores alone
+// fill most of the 80 registers, and that tier keeps two workgroups.
 template <int NT, int MAXP>
 __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_count_kernel(
     const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
@@ -1601,11 +1601,14 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
                             uint64_t* keepmask,
                             SipRow* rowinfo, int64_t* counts, PlanStatus* status, hipStream_t s) {
     const int64_t rows = B * H * QB;
-    // 512 threads per row, the scores of up to 32 pairs per thread in
-    // registers (rows of up to 32,768 blocks); longer rows re-read their
+    // 512 threads per row, the scores of up to 20 pairs per thread in
+    // registers (rows of up to 20,480 blocks); then 768 threads at 20 pairs
+    // (up to 30,720 blocks: 6 waves per SIMD where 512 threads at 24 or 32
+    // pairs run 4) and 512 at 32 (up to 32,768); longer rows re-read their
     // scores every pass. (Fewer threads per row, e.g. 320 at 30 pairs each
     // for the Wan2.1-like rows, was measured slower: 5.6 against 3.8 ms.)
-    const int64_t npass = ((M + 1) / 2 + 511) / 512;
+    const int64_t pairs = (M + 1) / 2;
+    const int64_t npass = (pairs + 511) / 512;
     return launch_checked([&] {
 #define ABSA_SIP_LAUNCH(NT, MP)                                                                  \
     hipLaunchKernelGGL((sip_count_kernel<NT, MP>), dim3(rows), dim3(NT), 0, s, scores, H, QB,   \
@@ -1613,7 +1616,7 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
         if (npass <= 8) ABSA_SIP_LAUNCH(512, 8);
         else if (npass <= 16) ABSA_SIP_LAUNCH(512, 16);
         else if (npass <= 20) ABSA_SIP_LAUNCH(512, 20);
-        else if (npass <= 24) ABSA_SIP_LAUNCH(512, 24);
+        else if (pairs <= 768 * 20) ABSA_SIP_LAUNCH(768, 20);
         else if (npass <= 32) ABSA_SIP_LAUNCH(512, 32);
         else ABSA_SIP_LAUNCH(512, 0);
 #undef ABSA_SIP_LAUNCH
