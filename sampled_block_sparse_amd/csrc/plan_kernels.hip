@@ -1605,8 +1605,10 @@ hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t Q
     // registers (rows of up to 20,480 blocks); then 768 threads at 20 pairs
     // (up to 30,720 blocks: 6 waves per SIMD where 512 threads at 24 or 32
     // pairs run 4) and 512 at 32 (up to 32,768); longer rows re-read their
-    // scores every pass. (Fewer threads per row, e.g. 320 at 30 pairs each
-    // for the Wan2.1-like rows, was measured slower: 5.6 against 3.8 ms.)
+    // scores every pass. (Other shapes for the Wan2.1-like rows of 18,900
+    // blocks were measured slower: 320 threads at 30 pairs 5.6 against
+    // 3.8 ms before later changes; 768 at 13 and 1024 at 10 pairs 2.50 and
+    // 2.73 against 2.35 ms.)
     const int64_t pairs = (M + 1) / 2;
     const int64_t npass = (pairs + 511) / 512;
     return launch_checked([&] {
