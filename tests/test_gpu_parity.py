@@ -358,14 +358,15 @@ def test_fill_queue_many_uncapped_blocks():
 
 
 @pytest.mark.parametrize("sampling", ["poisson", "systematic"])
-@pytest.mark.parametrize("M", [9001, 23000, 32765, 40002])
+@pytest.mark.parametrize("M", [9001, 18901, 23000, 32765, 40002])
 def test_sip_row_length_tiers(M, sampling):
     """The SIP count kernel keeps a row's scores in registers in tiers of
-    8, 16, 20, 24 or 32 block pairs per thread and re-reads them from memory
-    for longer rows; each wave owns one contiguous range of pairs, the last
-    one partly past the row's end. These lengths take the 16-, 24- and
-    32-pair tiers and the memory path (the video layers take 20 and 32), with
-    odd M. Rows alternate between heavy-tailed scores spread over the row
+    8, 16 or 20 block pairs per thread at 512 threads, 20 at 768 threads or
+    32 at 512, and re-reads them from memory for longer rows; each wave owns
+    one contiguous range of pairs, the last one partly past the row's end.
+    These lengths take the 16- and 20-pair tiers at 512 threads, the
+    768-thread tier, the 32-pair tier and the memory path (the video layers
+    take 512 x 20 and 768 x 20), with odd M. Rows alternate between heavy-tailed scores spread over the row
     and scores concentrated in one window (so that in later capping rounds
     most waves skip their pass). Sampled rows must match the oracle's SIP
     bit for bit."""
