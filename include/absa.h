@@ -91,7 +91,9 @@ typedef enum absa_sampling {
 /* Plan parameters. query_block must be 128 and kv_block 4 (the sizes the
  * pages give: [hamidun, IBCS paragraph] 128-query blocks, [hamidun, kernel
  * paragraph] KV blocks of at most 4 tokens). n_clusters in [1, 16]
- * (pages: 8); kmeans_iters in [1, 64] (pages: a fixed count, not stated;
+ * (pages: 8; the k-means keeps a row's centroids in registers and LDS and
+ * the score tiles take 32 centroid slots, so larger counts return
+ * ABSA_ERR_UNSUPPORTED); kmeans_iters in [1, 64] (pages: a fixed count, not stated;
  * default 4). budget_blocks = K, the KV blocks each query block samples in
  * expectation, in [1, N/4]. seed = the sampler's 64-bit Philox key; a plan
  * rebuilt at a later step takes a new seed. sampling = an absa_sampling
@@ -124,10 +126,17 @@ typedef enum absa_intermediate {
 absa_status absa_plan_params_init(absa_plan_params* out);
 
 /* Build a plan from Q and K: mean keys, IBCS k-means and scores, then SIP
- * probabilities, Philox draws and HT log-weights (steps 1-4 above).
+ * probabilities, Philox draws and HT log-weights (steps 1-4 above). The
+ * scores are within 1e-4 relative of their fp64 definition while the
+ * centroid logits |c.kbar| / sqrt(d) stay below about 300 (the score
+ * contraction runs on 22-bit block floating point operands, so its error
+ * grows with the largest logit of the 4 query blocks sharing a tile).
  * q, k: device [B, H, N, d] of dtype. On success *out owns device memory
- * until absa_plan_destroy. Blocks until the plan is complete (one
- * device-to-host read of the sampled block count sizes the plan). */
+ * until absa_plan_destroy. The call synchronises the stream twice: once to
+ * read the number of sampled blocks (the size of the plan's arrays, which
+ * the host allocates), and once when the plan is complete (the build's
+ * temporaries live in a per-device workspace that the next build reuses).
+ * It returns with the plan complete, usable on any stream. */
 absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype,
                              int64_t B, int64_t H, int64_t N, int64_t d,
                              const absa_plan_params* params, void* hip_stream,
@@ -165,6 +174,16 @@ absa_status absa_plan_info(absa_plan plan, int64_t* shape4, int64_t* rows,
 absa_status absa_plan_export(absa_plan plan, int64_t* rowptr, int32_t* idx,
                              float* logw, double* p);
 
+/* Device address of the plan's retained IBCS scores, float [B, H, QB, M]
+ * (QB = ceil(N/128), M = N/4, rows summing to 1), in *scores_dev; NULL when
+ * the plan was built without keep_intermediates or by
+ * absa_plan_from_scores / absa_plan_import. The memory belongs to the plan
+ * (valid until absa_plan_destroy; do not write to it). It can be handed to
+ * absa_plan_from_scores on the device, e.g. to draw a new plan from the
+ * same scores with another seed or budget [hamidun, kernel paragraph: a
+ * plan serves several steps]. ABSA_ERR_INVALID_ARG on NULL arguments. */
+absa_status absa_plan_scores(absa_plan plan, const float** scores_dev);
+
 /* Copy count elements starting at element offset of a retained intermediate
  * (see absa_intermediate) to host memory. ABSA_ERR_INVALID_ARG if the plan
  * did not keep intermediates or the range is out of bounds. Synchronous. */
@@ -177,7 +196,10 @@ absa_status absa_plan_export_intermediate(absa_plan plan, absa_intermediate whic
  * dtype. A row whose plan holds no block gets zeros. bf16 MFMA products,
  * fp32 accumulation and softmax. q, k and v must be finite: a NaN or an
  * infinity among them gives an unspecified output (no error is reported).
- * ABSA_ERR_PLAN_MISMATCH if the plan's (B, H, N, d) differ. */
+ * (B, H, N, d) restate the tensors' shape, which the plan fixes:
+ * ABSA_ERR_PLAN_MISMATCH if they differ from the plan's, so a tensor of
+ * another layer is caught before any kernel runs. fp32 inputs are first
+ * rounded to bf16 into temporaries from the library's memory pool. */
 absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k,
                                   const void* v, void* o, absa_dtype dtype,
                                   int64_t B, int64_t H, int64_t N, int64_t d,
@@ -189,9 +211,11 @@ absa_status absa_dense_attention(const void* q, const void* k, const void* v, vo
                                  absa_dtype dtype, int64_t B, int64_t H, int64_t N,
                                  int64_t d, void* hip_stream);
 
-/* Free a plan (NULL is a no-op). Waits for the plan's device to go idle,
- * then returns the plan's device memory to the library's pool for that
- * device (see absa_release_cached_memory). */
+/* Free a plan (NULL is a no-op). Does not wait: the plan's device memory
+ * goes back to the library's pool for that device (see
+ * absa_release_cached_memory) in stream order, after the latest attention
+ * call on the plan on each stream that used it. Work the caller queued on
+ * the plan by other routes (a captured graph) must be finished first. */
 void absa_plan_destroy(absa_plan plan);
 
 /* The library allocates plans from one stream-ordered memory pool per

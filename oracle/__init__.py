@@ -21,6 +21,8 @@ Steps, in the order the method applies them, and what pins each:
   kmeans_block        [hamidun, IBCS; edumints, three innovations]  pinned by
                       invariants, C=1 block mean, C=n self-clusters, planted
                       clusters and a hand-worked example
+  kmeans_tie_variants the same iteration with near-tie decisions taken the
+                      other way (test aid); pinned by a hand-worked exact tie
   ibcs_scores_row     [hamidun, IBCS]                      pinned by C=1 and C=n
                       reductions to library softmax, invariants, hand example
   sip_probabilities   [hamidun, SIP; edumints, three innovations]  pinned by
@@ -40,7 +42,8 @@ Steps, in the order the method applies them, and what pins each:
   dense_attention     textbook softmax attention; pinned against the library
                       scaled-dot-product attention on the CPU
 """
-from .ibcs import mean_keys, kmeans_block, ibcs_scores_row, ibcs_row, query_rows
+from .ibcs import (mean_keys, kmeans_block, kmeans_tie_variants, ibcs_scores_row, ibcs_row,
+                   query_rows)
 from .sip import (sip_probabilities, sip_draw_row, sip_uniforms, fixed_point_scores,
                   systematic_uniform, systematic_sizes, systematic_select,
                   systematic_draw_row, draw_row)
@@ -50,7 +53,7 @@ from .attention import (ht_attention_row, dense_attention, dense_attention_rows,
 from .plan import build_plan, plan_from_scores, ibcs_scores, plan_attention, OraclePlan
 
 __all__ = [
-    "mean_keys", "kmeans_block", "ibcs_scores_row", "ibcs_row", "query_rows",
+    "mean_keys", "kmeans_block", "kmeans_tie_variants", "ibcs_scores_row", "ibcs_row", "query_rows",
     "sip_probabilities", "sip_draw_row", "sip_uniforms", "fixed_point_scores",
     "systematic_uniform", "systematic_sizes", "systematic_select", "systematic_draw_row",
     "draw_row",

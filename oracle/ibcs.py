@@ -45,7 +45,8 @@ def mean_keys(K: np.ndarray, kv_block: int = 4) -> np.ndarray:
 
 
 def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4,
-                 return_margin: bool = False):
+                 return_margin: bool = False, override: dict | None = None,
+                 trace: list | None = None):
     """Lloyd k-means on the queries of one query block, in their original order.
 
     Qr: [n, d] float64 (n >= 1). Returns (centroids [C, d], weights [C],
@@ -56,6 +57,11 @@ def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4,
     smallest relative gap (second-nearest minus nearest, over nearest) seen
     in any assignment step: a gap near rounding level marks a decision that
     another summation order may take the other way.
+
+    override maps (iteration, query) to a cluster that the assignment of
+    that query in that iteration takes instead of its nearest one; trace, a
+    list, receives the [n, C_eff] squared distances of every iteration.
+    Both only serve kmeans_tie_variants; the default result ignores them.
     """
     n, d = Qr.shape
     if n < 1 or iters < 1 or n_clusters < 1:
@@ -65,10 +71,16 @@ def kmeans_block(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4,
     cent = Qr[start].copy()
     assign = np.zeros(n, dtype=np.int64)
     margin = np.inf
-    for _ in range(iters):
+    for it in range(iters):
         diff = Qr[:, None, :] - cent[None, :, :]           # [n, C_eff, d]
         dist2 = np.einsum("ncd,ncd->nc", diff, diff)
         assign = np.argmin(dist2, axis=1)                  # first minimum wins
+        if trace is not None:
+            trace.append(dist2)
+        if override:
+            for (oit, i), m in override.items():
+                if oit == it:
+                    assign[i] = m
         if return_margin and c_eff > 1:
             srt = np.sort(dist2, axis=1)
             gap = (srt[:, 1] - srt[:, 0]) / np.maximum(srt[:, 0], 1e-300)
@@ -109,3 +121,42 @@ def ibcs_row(Qr: np.ndarray, kbar: np.ndarray, n_clusters: int = 8, iters: int =
     """k-means then scores for one query block; returns (scores, centroids, weights)."""
     cent, w, _ = kmeans_block(Qr, n_clusters, iters)
     return ibcs_scores_row(cent, w, kbar, Qr.shape[1]), cent, w
+
+
+def kmeans_tie_variants(Qr: np.ndarray, n_clusters: int = 8, iters: int = 4,
+                        rel_tol: float = 1e-12, limit: int = 64):
+    """Every result the Lloyd iteration of kmeans_block reaches when each
+    assignment decided by a near-tie may go either way.
+
+    A query whose two nearest centroids lie within a relative gap rel_tol of
+    each other ((second - nearest) / nearest) has a decision that another
+    summation order can take the other way, with either outcome a correct
+    reading of the rule. Starting from the plain run, each such decision
+    (taken in order of iteration, then query) is branched to the
+    second-nearest cluster and the iteration re-run from it. Returns a list
+    of (centroids, weights, override) with the plain result first, at most
+    `limit` entries.
+    """
+    out = []
+    stack = [{}]
+    while stack and len(out) < limit:
+        ov = stack.pop()
+        trace = []
+        cent, w, _ = kmeans_block(Qr, n_clusters, iters, override=ov, trace=trace)
+        out.append((cent, w, dict(ov)))
+        last = max(ov) if ov else (-1, -1)
+        for it, dist2 in enumerate(trace):
+            if dist2.shape[1] < 2 or it < last[0]:
+                continue
+            order = np.argsort(dist2, axis=1, kind="stable")
+            near = dist2[np.arange(dist2.shape[0]), order[:, 0]]
+            second = dist2[np.arange(dist2.shape[0]), order[:, 1]]
+            gap = (second - near) / np.maximum(near, 1e-300)
+            for i in np.nonzero(gap < rel_tol)[0]:
+                key = (it, int(i))
+                if key <= last:
+                    continue
+                branch = dict(ov)
+                branch[key] = int(order[i, 1])
+                stack.append(branch)
+    return out

@@ -9,6 +9,7 @@ The functions carry the C names:
   absa_plan_create(q, k, budget_blocks, seed, ...) -> Plan
   absa_plan_from_scores(scores, N, d, budget_blocks, seed, sampling=...) -> Plan
   absa_plan_import(rowptr, idx, logw, p, B, H, N, d) -> Plan
+  absa_plan_scores(plan) -> device address of the retained scores, or 0
   absa_sparse_attention(plan, q, k, v, out=None) -> out
   absa_dense_attention(q, k, v, out=None) -> out
 Tensors are torch CUDA (HIP) tensors, contiguous [B, H, N, d], bfloat16 or
@@ -24,7 +25,8 @@ import torch
 
 __all__ = [
     "AbsaError", "Plan", "absa_plan_create", "absa_plan_from_scores", "absa_plan_import",
-    "absa_sparse_attention", "absa_dense_attention", "absa_status_string", "absa_last_error",
+    "absa_plan_scores", "absa_sparse_attention",
+    "absa_dense_attention", "absa_status_string", "absa_last_error",
     "get_lib", "LIB_PATH", "ABSA_OK", "ABSA_ERR_INVALID_ARG", "ABSA_ERR_UNSUPPORTED",
     "ABSA_ERR_OUT_OF_MEMORY", "ABSA_ERR_DEVICE", "ABSA_ERR_PLAN_MISMATCH",
     "INTER_MEAN_KEYS", "INTER_CENTROIDS", "INTER_WEIGHTS", "INTER_SCORES",
@@ -91,6 +93,7 @@ def get_lib():
         "absa_plan_info": (_i32, [_vp, _vp, _vp, _vp, _vp]),
         "absa_plan_export": (_i32, [_vp, _vp, _vp, _vp, _vp]),
         "absa_plan_export_intermediate": (_i32, [_vp, _i32, _i64, _i64, _vp]),
+        "absa_plan_scores": (_i32, [_vp, ctypes.POINTER(_vp)]),
         "absa_sparse_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
                                          _i64, _vp]),
         "absa_dense_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp]),
@@ -242,40 +245,75 @@ def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed:
     return Plan(out.value)
 
 
-def absa_plan_from_scores(scores: torch.Tensor, N: int, d: int, budget_blocks: int, seed: int,
-                          sampling="poisson", stream=None) -> Plan:
-    if scores.dtype != torch.float32 or scores.dim() != 4:
-        raise ValueError("scores must be float32 [B, H, QB, M]")
-    B, H = int(scores.shape[0]), int(scores.shape[1])
-    if tuple(scores.shape[2:]) != ((N + 127) // 128, N // 4):
-        raise ValueError("scores must be [B, H, ceil(N/128), N/4]")
+def absa_plan_from_scores(scores, N: int, d: int, budget_blocks: int, seed: int,
+                          sampling="poisson", stream=None, B: int | None = None,
+                          H: int | None = None) -> Plan:
+    """scores: a float32 GPU tensor [B, H, ceil(N/128), N/4], or the device
+    address (int) of such an array, e.g. from absa_plan_scores, with B and H
+    given."""
+    if isinstance(scores, int):
+        if B is None or H is None or not scores:
+            raise ValueError("a device address needs B and H (and must not be 0)")
+        ptr = _vp(scores)
+    else:
+        if scores.dtype != torch.float32 or scores.dim() != 4:
+            raise ValueError("scores must be float32 [B, H, QB, M]")
+        B, H = int(scores.shape[0]), int(scores.shape[1])
+        if tuple(scores.shape[2:]) != ((N + 127) // 128, N // 4):
+            raise ValueError("scores must be [B, H, ceil(N/128), N/4]")
+        ptr = _dev(scores, "scores")
     out = _vp()
-    _check(get_lib().absa_plan_from_scores(_dev(scores, "scores"), B, H, N, d, budget_blocks,
+    _check(get_lib().absa_plan_from_scores(ptr, B, H, N, d, budget_blocks,
                                            seed & 0xFFFFFFFFFFFFFFFF, _sampling_code(sampling),
                                            _stream(stream), ctypes.byref(out)))
     return Plan(out.value)
 
 
 def absa_plan_import(rowptr, idx, logw, p, B: int, H: int, N: int, d: int, stream=None) -> Plan:
+    """Plan from a host CSR. The C call reads rowptr[0..rows] and then
+    rowptr[rows] entries of idx, logw and p, so their lengths are checked
+    here first (rows = B*H*ceil(N/128))."""
+    rows = B * H * ((N + 127) // 128)
     rowptr, rp = _host(rowptr, np.int64)
+    if rowptr.ndim != 1 or rowptr.size != rows + 1:
+        raise ValueError(f"rowptr must hold rows + 1 = {rows + 1} entries (got {rowptr.size})")
+    nnz = int(rowptr[-1])
     idx, ip = _host(idx, np.int32)
     logw, lp = _host(logw, np.float32)
+    for name, a in (("idx", idx), ("logw", logw)):
+        if a.ndim != 1 or a.size != nnz:
+            raise ValueError(f"{name} must hold rowptr[-1] = {nnz} entries (got {a.size})")
     pp = _vp()
     if p is not None:
         p, pp = _host(p, np.float64)
+        if p.ndim != 1 or p.size != nnz:
+            raise ValueError(f"p must hold rowptr[-1] = {nnz} entries (got {p.size})")
     out = _vp()
     _check(get_lib().absa_plan_import(rp, ip, lp, pp, B, H, N, d, _stream(stream),
                                       ctypes.byref(out)))
     return Plan(out.value)
 
 
-def absa_sparse_attention(plan: Plan, q, k, v, out=None, stream=None):
+def absa_plan_scores(plan: Plan) -> int:
+    """Device address of the plan's retained scores [B, H, QB, M] (float32),
+    or 0 when the plan did not keep them."""
+    ptr = _vp()
+    _check(get_lib().absa_plan_scores(plan.handle, ctypes.byref(ptr)))
+    return ptr.value or 0
+
+
+def _attention_args(q, k, v, out):
     B, H, N, d = _shape4(q)
     if out is None:
         out = torch.empty_like(q)
     for t, nm in ((k, "k"), (v, "v"), (out, "out")):
         if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
             raise ValueError(f"{nm} must match q in shape and dtype")
+    return B, H, N, d, out
+
+
+def absa_sparse_attention(plan: Plan, q, k, v, out=None, stream=None):
+    B, H, N, d, out = _attention_args(q, k, v, out)
     _check(get_lib().absa_sparse_attention(plan.handle, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                            _dev(out, "out"), _dtype_code(q), B, H, N, d,
                                            _stream(stream)))
@@ -283,12 +321,7 @@ def absa_sparse_attention(plan: Plan, q, k, v, out=None, stream=None):
 
 
 def absa_dense_attention(q, k, v, out=None, stream=None):
-    B, H, N, d = _shape4(q)
-    if out is None:
-        out = torch.empty_like(q)
-    for t, nm in ((k, "k"), (v, "v"), (out, "out")):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
-            raise ValueError(f"{nm} must match q in shape and dtype")
+    B, H, N, d, out = _attention_args(q, k, v, out)
     _check(get_lib().absa_dense_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                           _dev(out, "out"), _dtype_code(q), B, H, N, d,
                                           _stream(stream)))

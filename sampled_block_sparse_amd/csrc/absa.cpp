@@ -33,6 +33,16 @@ struct absa_plan_s {
     float* cent = nullptr;
     float* w = nullptr;
     float* scores = nullptr;
+    // The streams of the plan's attention calls, each with an event recorded
+    // after its latest call: destroy releases the buffers in stream order
+    // after all of them. The events are created with the plan, so recording
+    // one allocates nothing; a fifth stream takes the oldest slot once that
+    // slot's work has finished.
+    static constexpr int kUseSlots = 4;
+    std::mutex use_mutex;
+    hipStream_t use_stream[kUseSlots] = {};
+    hipEvent_t use_event[kUseSlots] = {};
+    int n_use = 0, next_evict = 0;
 };
 
 namespace {
@@ -408,24 +418,76 @@ void keep(DeviceArena& arena, absa_plan_s* P) {
     arena.release(P->scores);
 }
 
-// Waits for the plan's device to go idle, then returns the plan's buffers to
-// that device's pool.
+// Returns the plan's buffers to its device's pool in stream order: the
+// library's side stream waits for the event of every stream that ran an
+// attention call on the plan, then frees them. Nothing waits on the host.
+// (Without the side stream, which only fails if a stream cannot be created,
+// it waits for those events on the host and frees on the null stream.)
 void free_plan(absa_plan_s* P) {
     if (!P) return;
     int cur = 0;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
     if (!have_cur || cur != P->device) (void)hipSetDevice(P->device);
-    (void)hipDeviceSynchronize();
+    hipStream_t side = nullptr;
+    if (device_side_stream(&side) != ABSA_OK) side = nullptr;
+    for (int i = 0; i < P->n_use; ++i) {
+        if (side) (void)hipStreamWaitEvent(side, P->use_event[i], 0);
+        else (void)hipEventSynchronize(P->use_event[i]);
+    }
     void* bufs[] = {P->rowptr, P->idx, P->logw, P->p, P->kbar, P->cent, P->w, P->scores};
     for (void* b : bufs)
-        if (b) (void)hipFreeAsync(b, nullptr);
+        if (b) (void)hipFreeAsync(b, side);
+    // an event destroyed while a wait on it is queued is released once the
+    // wait has passed
+    for (hipEvent_t e : P->use_event)
+        if (e) (void)hipEventDestroy(e);
     if (have_cur && cur != P->device) (void)hipSetDevice(cur);
     delete P;
 }
 
+// Create the plan's use events (see absa_plan_s).
+absa_status create_use_events(absa_plan_s* P) {
+    for (hipEvent_t& e : P->use_event)
+        ABSA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "plan use event");
+    return ABSA_OK;
+}
+
+// Record that stream s ran work on the plan. Under stream capture nothing is
+// recorded: the captured graph's launches are ordered by the caller, who
+// must keep the plan alive while they may run.
+absa_status note_use(absa_plan_s* P, hipStream_t s) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    ABSA_HIP(hipStreamIsCapturing(s, &cap), "stream capture status");
+    if (cap != hipStreamCaptureStatusNone) return ABSA_OK;
+    std::lock_guard<std::mutex> lock(P->use_mutex);
+    int slot = -1;
+    for (int i = 0; i < P->n_use; ++i)
+        if (P->use_stream[i] == s) slot = i;
+    if (slot < 0) {
+        if (P->n_use < absa_plan_s::kUseSlots) {
+            slot = P->n_use++;
+        } else {
+            slot = P->next_evict;
+            P->next_evict = (slot + 1) % absa_plan_s::kUseSlots;
+            ABSA_HIP(hipEventSynchronize(P->use_event[slot]), "wait for an earlier use");
+        }
+        P->use_stream[slot] = s;
+    }
+    ABSA_HIP(hipEventRecord(P->use_event[slot], s), "record plan use");
+    return ABSA_OK;
+}
+
 absa_status set_plan_device(absa_plan_s* P) {
     ABSA_HIP(hipGetDevice(&P->device), "current device");
-    return ABSA_OK;
+    return create_use_events(P);
+}
+
+// Release a plan whose build failed: its buffers went back with the build's
+// arena, only the events are left.
+void discard_plan(absa_plan_s* P) {
+    for (hipEvent_t e : P->use_event)
+        if (e) (void)hipEventDestroy(e);
+    delete P;
 }
 
 }  // namespace
@@ -535,7 +597,7 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     if (st != ABSA_OK) {
         P->rowptr = nullptr; P->idx = nullptr; P->logw = nullptr; P->p = nullptr;
         P->kbar = P->cent = P->w = P->scores = nullptr;
-        delete P;
+        discard_plan(P);
         return st;
     }
     *out = P;
@@ -575,7 +637,7 @@ absa_status absa_plan_from_scores(const float* scores_dev, int64_t B, int64_t H,
         return ABSA_OK;
     }();
     if (st != ABSA_OK) {
-        delete P;
+        discard_plan(P);
         return st;
     }
     *out = P;
@@ -589,8 +651,9 @@ absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx, const fl
     *out = nullptr;
     if (!rowptr) return fail(ABSA_ERR_INVALID_ARG, "rowptr is NULL");
     ABSA_TRY(check_shape(B, H, N, d));
-    absa_plan_s tmp;
-    fill_dims(&tmp, B, H, N, d);
+    struct { int64_t rows, M; } tmp;
+    tmp.M = N / kKvBlock;
+    tmp.rows = B * H * ((N + kQueryBlock - 1) / kQueryBlock);
     if (rowptr[0] != 0) return fail(ABSA_ERR_INVALID_ARG, "rowptr[0] must be 0");
     for (int64_t i = 0; i < tmp.rows; ++i) {
         const int64_t lo = rowptr[i], hi = rowptr[i + 1];
@@ -616,7 +679,7 @@ absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx, const fl
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     absa_plan_s* P = new (std::nothrow) absa_plan_s();
     if (!P) return fail(ABSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
-    *P = tmp;
+    fill_dims(P, B, H, N, d);
     P->nnz = nnz;
     absa_status st = [&]() -> absa_status {
         ABSA_TRY(set_plan_device(P));
@@ -647,7 +710,7 @@ absa_status absa_plan_import(const int64_t* rowptr, const int32_t* idx, const fl
         return ABSA_OK;
     }();
     if (st != ABSA_OK) {
-        delete P;
+        discard_plan(P);
         return st;
     }
     *out = P;
@@ -752,7 +815,9 @@ absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k, 
                     "plan built for (B,H,N,d) = (%lld,%lld,%lld,%lld), called with (%lld,%lld,%lld,%lld)",
                     (long long)plan->B, (long long)plan->H, (long long)plan->N, (long long)plan->d,
                     (long long)B, (long long)H, (long long)N, (long long)d);
-    return run_attention(q, k, v, o, dtype, B, H, N, d, plan, static_cast<hipStream_t>(hip_stream));
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ABSA_TRY(run_attention(q, k, v, o, dtype, B, H, N, d, plan, s));
+    return note_use(plan, s);
 }
 
 absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
@@ -761,6 +826,12 @@ absa_status absa_dense_attention(const void* q, const void* k, const void* v, vo
     ABSA_TRY(attention_common(q, k, v, o, dtype, B, H, N, d));
     return run_attention(q, k, v, o, dtype, B, H, N, d, nullptr,
                          static_cast<hipStream_t>(hip_stream));
+}
+
+absa_status absa_plan_scores(absa_plan plan, const float** scores_dev) {
+    if (!plan || !scores_dev) return fail(ABSA_ERR_INVALID_ARG, "plan and scores_dev must be non-NULL");
+    *scores_dev = plan->scores;
+    return ABSA_OK;
 }
 
 void absa_plan_destroy(absa_plan plan) {

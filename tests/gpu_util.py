@@ -53,16 +53,78 @@ def oracle_plan_of(gp: dict, B, H, N, d) -> oracle.OraclePlan:
     return oracle.OraclePlan(B, H, N, d, M, QB, gp["rowptr"], gp["idx"], gp["logw"], gp["p"])
 
 
-def flips_explained(Q64, rows_bad, N, C, T, margin_tol=1e-9):
-    """True if every row whose cluster weights differ had a near-tie in the
-    oracle's assignment (so either side's decision is a correct reading)."""
+# Relative margin (second-nearest minus nearest squared distance, over the
+# nearest) below which an assignment may go either way: the oracle sums
+# (q - c)^2 and the kernel |c|^2 - 2 q.c, both in fp64, and their rounding
+# differs by a few units of 2^-52 of |q|^2 + |c|^2, far below this.
+KMEANS_TIE_REL = 1e-12
+CENT_TOL = 1e-6        # centroids: fp32 rounding of the fp64 member means
+
+
+def _cluster_match(w_gpu, c_gpu, w_ref, c_ref):
+    return (np.array_equal(w_gpu, w_ref.astype(np.float32)) and
+            np.abs(c_gpu - c_ref).max() <= CENT_TOL * max(1.0, float(np.abs(c_ref).max())))
+
+
+def clustering_references(Q64, w_gpu, c_gpu, ref_w, ref_c, N, C, T, what=""):
+    """The oracle clustering each row of the GPU's result equals.
+
+    A row matches the plain oracle run when its weights are the same fp32
+    values (counts over n) and its centroids lie within fp32 rounding of the
+    oracle's member means. A row that does not is accepted only if the
+    oracle saw a near-tie (relative margin below KMEANS_TIE_REL) and the GPU's
+    weights and centroids equal the oracle run with that decision taken the
+    other way (oracle.kmeans_tie_variants): then they are the counts and
+    member means of an assignment the rule admits. Asserts that every row
+    matches; returns (weights [rows, C], centroids [rows, C, d]) of the
+    matching runs and the list of flipped rows. Prints the number of flips.
+    """
     B, H = Q64.shape[0], Q64.shape[1]
     QB = (N + 127) // 128
-    for row in rows_bad:
-        bh, r = divmod(int(row), QB)
+    rows = B * H * QB
+    w_gpu = w_gpu.reshape(rows, C)
+    c_gpu = c_gpu.reshape(rows, C, -1)
+    out_w = ref_w.reshape(rows, C).copy()
+    out_c = ref_c.reshape(rows, C, -1).copy()
+    flipped = []
+    for row in range(rows):
+        if _cluster_match(w_gpu[row], c_gpu[row], out_w[row], out_c[row]):
+            continue
+        bh, r = divmod(row, QB)
         b, h = divmod(bh, H)
         lo, hi = r * 128, min(r * 128 + 128, N)
-        *_, margin = oracle.kmeans_block(Q64[b, h, lo:hi], C, T, return_margin=True)
-        if margin > margin_tol:
-            return False
-    return True
+        variants = oracle.kmeans_tie_variants(Q64[b, h, lo:hi], C, T, KMEANS_TIE_REL)
+        hit = [v for v in variants[1:] if _cluster_match(w_gpu[row], c_gpu[row], v[1], v[0])]
+        assert hit, (f"{what}: row {row} clusters differ from the oracle's and from every "
+                     f"near-tie variant ({len(variants) - 1} variants)")
+        out_c[row], out_w[row] = hit[0][0], hit[0][1]
+        flipped.append(row)
+    print(f"{what}: rows whose k-means took the other side of a near-tie: {len(flipped)} "
+          f"of {rows}")
+    return out_w, out_c, flipped
+
+
+def row_clustering_reference(Qr, w_gpu, c_gpu, C, T, what=""):
+    """clustering_references for one row given its queries Qr [n, d]:
+    returns (centroids, weights, flipped)."""
+    variants = oracle.kmeans_tie_variants(Qr, C, T, KMEANS_TIE_REL)
+    for i, (c, w, _) in enumerate(variants):
+        if _cluster_match(w_gpu.reshape(C), c_gpu.reshape(C, -1), w, c):
+            return c, w, i > 0
+    raise AssertionError(f"{what}: clusters differ from the oracle's and from every near-tie "
+                         f"variant ({len(variants) - 1} variants)")
+
+
+def reference_scores(K64, ref_w, ref_c, rows_idx, N, H):
+    """Oracle scores of the given rows from the given clusterings."""
+    QB = (N + 127) // 128
+    d = K64.shape[-1]
+    out = {}
+    kb = {}
+    for row in rows_idx:
+        bh, r = divmod(int(row), QB)
+        b, h = divmod(bh, H)
+        if (b, h) not in kb:
+            kb[(b, h)] = oracle.mean_keys(K64[b, h])
+        out[int(row)] = oracle.ibcs_scores_row(ref_c[row], ref_w[row], kb[(b, h)], d)
+    return out

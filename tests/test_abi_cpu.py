@@ -25,7 +25,8 @@ def test_header_declares_the_interface():
     for required in ("absa_plan_create", "absa_plan_from_scores", "absa_plan_import",
                      "absa_plan_info", "absa_plan_export", "absa_plan_export_intermediate",
                      "absa_sparse_attention", "absa_dense_attention", "absa_plan_destroy",
-                     "absa_status_string", "absa_last_error", "absa_plan_params_init"):
+                     "absa_status_string", "absa_last_error", "absa_plan_params_init",
+                     "absa_plan_scores"):
         assert required in names
 
 
@@ -137,6 +138,8 @@ def test_other_calls_reject_before_device_work():
     assert lib.absa_plan_info(None, None, None, None, None) == absa.ABSA_ERR_INVALID_ARG
     assert lib.absa_plan_export(None, None, None, None, None) == absa.ABSA_ERR_INVALID_ARG
     assert lib.absa_plan_export_intermediate(None, 0, 0, 0, None) == absa.ABSA_ERR_INVALID_ARG
+    ptr = ctypes.c_void_p(7)
+    assert lib.absa_plan_scores(None, ctypes.byref(ptr)) == absa.ABSA_ERR_INVALID_ARG
     lib.absa_plan_destroy(None)     # no-op
 
 
@@ -172,3 +175,28 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         absa.absa_dense_attention(q, q, q)
+
+
+@pytest.mark.parametrize("what", ["short rowptr", "long rowptr", "short idx", "short logw",
+                                  "short p"])
+def test_binding_checks_import_lengths(what):
+    """The C import reads rowptr[0..rows] and rowptr[rows] entries of the
+    other arrays (it has no length arguments): the binding rejects arrays of
+    the wrong length before calling it. B=1, H=2, N=256: rows = 4."""
+    import numpy as np
+    rowptr = np.array([0, 2, 3, 3, 5], np.int64)
+    idx = np.array([0, 5, 1, 7, 9], np.int32)
+    logw = np.zeros(5, np.float32)
+    p = np.ones(5)
+    if what == "short rowptr":
+        rowptr = rowptr[:3]
+    elif what == "long rowptr":
+        rowptr = np.append(rowptr, 5)
+    elif what == "short idx":
+        idx = idx[:4]
+    elif what == "short logw":
+        logw = logw[:2]
+    else:
+        p = p[:4]
+    with pytest.raises(ValueError):
+        absa.absa_plan_import(rowptr, idx, logw, p, 1, 2, 256, 64)

@@ -10,8 +10,8 @@ import torch
 import oracle
 import sampled_block_sparse_amd as absa
 import synth
-from tests.gpu_util import (SCORE_REL, check_output, check_plan_exact, flips_explained,
-                            oracle_plan_of, score_error, to64, ulp_diff_f32)
+from tests.gpu_util import (SCORE_REL, check_output, check_plan_exact, clustering_references,
+                            oracle_plan_of, reference_scores, score_error, to64, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,9 @@ CASES = {
     "ragged_d64_f32": (dict(B=1, H=2, N=1340, d=64, dtype="f32", seed=6), ("pct", 20)),
     "ragged_d128_f32": (dict(B=1, H=2, N=700, d=128, dtype="f32", seed=8), ("pct", 15)),
     "short_rows": (dict(B=1, H=2, N=200, d=128, seed=7), ("blocks", 3)),
+    # bf16 output at d = 64 over several key tiles (75 blocks: 5 tiles, the
+    # last one partial) and a partial last query block
+    "multi_d64_bf16": (dict(B=1, H=2, N=3000, d=64, seed=23), ("pct", 10)),
 }
 
 
@@ -110,20 +113,19 @@ def test_plan_create_stages_and_output(case):
     kbar = plan.export_intermediate(absa.INTER_MEAN_KEYS).reshape(B, H, M, d)
     ref_kbar = oracle.mean_keys(c["K"])
     assert np.abs(kbar - ref_kbar).max() <= 2.0 ** -22 * max(1.0, np.abs(c["K"]).max())
-    # cluster weights (exact) and centroids (fp32 rounding of the fp64 means)
-    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8).reshape(B * H * QB, 8)
-    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * 8 * d).reshape(
-        B * H * QB, 8, d)
-    ref_w = c["wts"].reshape(-1, 8).astype(np.float32)
-    bad = np.nonzero((w != ref_w).any(axis=1))[0]
-    assert flips_explained(c["Q"], bad, N, 8, 4), f"weights differ in rows {bad[:10]}"
-    good = np.setdiff1d(np.arange(B * H * QB), bad)
-    ref_c = c["cents"].reshape(-1, 8, d)
-    assert np.abs(cen[good] - ref_c[good]).max() <= 1e-6 * max(1.0, np.abs(ref_c).max())
-    # scores within the stated relative tolerance
+    # cluster weights (exact) and centroids (fp32 rounding of the fp64 means),
+    # each row those of the oracle's run or of a validated near-tie variant
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8)
+    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * 8 * d)
+    ref_w, ref_c, flipped = clustering_references(c["Q"], w, cen, c["wts"], c["cents"], N, 8, 4,
+                                                  c["name"])
+    # scores within the stated relative tolerance, on every row
     s = plan.export_intermediate(absa.INTER_SCORES).reshape(B * H * QB, M)
-    err = score_error(s[good], c["scores"].reshape(-1, M)[good])
-    print(f"score error max {err.max():.3e}; rows with assignment near-ties: {len(bad)}")
+    ref_s = c["scores"].reshape(-1, M).copy()
+    for row, sc in reference_scores(c["K"], ref_w, ref_c, flipped, N, H).items():
+        ref_s[row] = sc
+    err = score_error(s, ref_s)
+    print(f"score error max {err.max():.3e}")
     assert err.max() <= SCORE_REL
     # the plan is the SIP rule applied to the GPU's own fp32 scores
     gp = plan.export()
@@ -182,12 +184,14 @@ def test_cluster_and_iteration_variants(C, T):
     plan = absa.absa_plan_create(q.to(DEV), k.to(DEV), 30, 99, n_clusters=C, kmeans_iters=T,
                                  keep_intermediates=True)
     s = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M)
-    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * C).reshape(-1, C)
-    ref_s, _, ref_w = oracle.ibcs_scores(Q, K, n_clusters=C, iters=T)
-    bad = np.nonzero((w != ref_w.reshape(-1, C).astype(np.float32)).any(axis=1))[0]
-    assert flips_explained(Q, bad, N, C, T)
-    good = np.setdiff1d(np.arange(B * H * QB), bad)
-    assert score_error(s[good], ref_s.reshape(-1, M)[good]).max() <= SCORE_REL
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * C)
+    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * C * d)
+    ref_s, ref_c, ref_w = oracle.ibcs_scores(Q, K, n_clusters=C, iters=T)
+    ref_w, ref_c, flipped = clustering_references(Q, w, cen, ref_w, ref_c, N, C, T, f"C={C} T={T}")
+    ref_s = ref_s.reshape(-1, M)
+    for row, sc in reference_scores(K, ref_w, ref_c, flipped, N, H).items():
+        ref_s[row] = sc
+    assert score_error(s, ref_s).max() <= SCORE_REL
 
 
 def test_score_magnitude_spread():
@@ -209,13 +213,52 @@ def test_score_magnitude_spread():
     plan = absa.absa_plan_create(qt.to(DEV), kt.to(DEV), 26, 3, keep_intermediates=True)
     s = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M)
     QB = (N + 127) // 128
-    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8).reshape(-1, 8)
-    ref_s, _, ref_w = oracle.ibcs_scores(Q, K)
-    bad = np.nonzero((w != ref_w.reshape(-1, 8).astype(np.float32)).any(axis=1))[0]
-    assert flips_explained(Q, bad, N, 8, 4)
-    good = np.setdiff1d(np.arange(B * H * QB), bad)
-    err = score_error(s[good], ref_s.reshape(-1, M)[good])
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8)
+    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * 8 * d)
+    ref_s, ref_c, ref_w = oracle.ibcs_scores(Q, K)
+    ref_w, ref_c, flipped = clustering_references(Q, w, cen, ref_w, ref_c, N, 8, 4, "spread")
+    ref_s = ref_s.reshape(-1, M)
+    for row, sc in reference_scores(K, ref_w, ref_c, flipped, N, H).items():
+        ref_s[row] = sc
+    err = score_error(s, ref_s)
     print(f"score error max {err.max():.3e}")
+    assert err.max() <= SCORE_REL
+
+
+@pytest.mark.parametrize("max_logit", [100, 200])
+def test_score_large_logits(max_logit):
+    """Centroid logits c.kbar/sqrt(d) reaching 100 and 200, with the query
+    blocks of each wave of the score kernel alternating between full-norm
+    and 1/8-norm queries (the 4 query blocks of a wave share one block
+    floating point exponent, so the small ones are quantised against the
+    large ones). The scores must still meet 1e-4. (Measured: about 2e-5 at
+    a logit of 100 and 3e-5 at 200; 8.6e-5 at 300, the documented limit.)"""
+    q, k, _ = synth.make_inputs("small")
+    s = float(np.sqrt(max_logit / 24.5))       # the unscaled layer reaches about 24.5
+    fac = torch.ones(2048)
+    for r in range(16):
+        if r % 4 in (2, 3):
+            fac[128 * r:128 * r + 128] = 1.0 / 8
+    q = (q[:, :2, :2048].float() * s * fac[None, None, :, None]).to(torch.bfloat16)
+    k = (k[:, :2, :2048].float() * s).to(torch.bfloat16)
+    Q, K = to64(q), to64(k)
+    B, H, N, d = q.shape
+    M, QB = N // 4, (N + 127) // 128
+    plan = absa.absa_plan_create(q.to(DEV), k.to(DEV), 51, 3, keep_intermediates=True)
+    sg = plan.export_intermediate(absa.INTER_SCORES).reshape(-1, M)
+    w = plan.export_intermediate(absa.INTER_WEIGHTS, 0, B * H * QB * 8)
+    cen = plan.export_intermediate(absa.INTER_CENTROIDS, 0, B * H * QB * 8 * d)
+    ref_s, ref_c, ref_w = oracle.ibcs_scores(Q, K)
+    kb = oracle.mean_keys(K)
+    top = max(float(np.abs(ref_c[0, h, r] @ kb[0, h].T).max()) / np.sqrt(d)
+              for h in range(H) for r in range(QB))
+    assert 0.9 * max_logit < top < 1.1 * max_logit
+    ref_w, ref_c, flipped = clustering_references(Q, w, cen, ref_w, ref_c, N, 8, 4, "large")
+    ref_s = ref_s.reshape(-1, M)
+    for row, sc in reference_scores(K, ref_w, ref_c, flipped, N, H).items():
+        ref_s[row] = sc
+    err = score_error(sg, ref_s)
+    print(f"max logit {top:.1f}: score error max {err.max():.3e}")
     assert err.max() <= SCORE_REL
 
 
@@ -463,3 +506,58 @@ def _subplan(gp, H, hs, N):
             rowptr.append(rowptr[-1] + hi - lo)
     return (np.array(rowptr, np.int64), np.concatenate(idx), np.concatenate(logw),
             np.concatenate(p))
+
+
+def test_plan_scores_on_device_give_the_same_plan():
+    """absa_plan_scores hands the retained device scores of a plan to
+    absa_plan_from_scores with no host copy: with the same budget, seed and
+    design the new plan equals the first bit for bit (both designs). A plan
+    without intermediates has no scores (address 0)."""
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=3, N=2000, d=128, seed=31))
+    B, H, N, d = q.shape
+    for sampling in ("poisson", "systematic"):
+        plan = absa.absa_plan_create(q, k, 60, 41, keep_intermediates=True, sampling=sampling)
+        ptr = absa.absa_plan_scores(plan)
+        assert ptr != 0
+        again = absa.absa_plan_from_scores(ptr, N, d, 60, 41, sampling=sampling, B=B, H=H)
+        a, b = plan.export(), again.export()
+        for key in a:
+            assert np.array_equal(a[key], b[key]), (sampling, key)
+        # another budget from the same device scores is the oracle's SIP on them
+        s = plan.export_intermediate(absa.INTER_SCORES).reshape(B, H, (N + 127) // 128, N // 4)
+        other = absa.absa_plan_from_scores(ptr, N, d, 25, 7, sampling=sampling, B=B, H=H)
+        check_plan_exact(other.export(), oracle.plan_from_scores(s, B, H, N, d, 25, 7, sampling),
+                         f"scores reused, {sampling}")
+        plan.destroy()
+    plain = absa.absa_plan_create(q, k, 60, 41)
+    assert absa.absa_plan_scores(plain) == 0
+
+
+def test_destroy_is_stream_ordered():
+    """absa_plan_destroy does not wait: the plan's memory returns to the
+    pool after the attention calls queued on it, on every stream that used
+    it. Plans are destroyed right after queuing attention on two side
+    streams, new plans (which may reuse that memory) are built at once, and
+    the queued outputs must still be the ones computed with the plan alive."""
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=4, N=8192, d=128, seed=32))
+    ref_plan = absa.absa_plan_create(q, k, 200, 9)
+    ref = absa.absa_sparse_attention(ref_plan, q, k, v)
+    torch.cuda.synchronize()
+    ref_plan.destroy()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        plan = absa.absa_plan_create(q, k, 200, 9)
+        outs = []
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                o = torch.empty_like(q)
+                absa.absa_sparse_attention(plan, q, k, v, o, stream=st)
+                outs.append(o)
+        plan.destroy()
+        junk = [absa.absa_plan_create(q, k, 300, 100 + rep + i) for i in range(2)]
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o, ref), f"rep {rep}"
+        for j in junk:
+            j.destroy()

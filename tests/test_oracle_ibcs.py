@@ -159,3 +159,38 @@ def test_full_scores_shapes_and_rows():
     # the partial last block (72 queries) is clustered on its own queries only
     c, w, _ = oracle.kmeans_block(Q[0, 1, 128:200], 8, 4)
     np.testing.assert_array_equal(C[0, 1, 1], c)
+
+
+def test_kmeans_tie_variants_hand_example():
+    """Queries 0, 2, 1 on a line with C = 2 and T = 1: the initial centroids
+    are q[0] = 0 and q[1] = 2, and q[2] = 1 is exactly as far from both. The
+    rule gives it to cluster 0 (weights 2/3, 1/3; centroids 0.5 and 2); the
+    other side of the tie gives it to cluster 1 (weights 1/3, 2/3; centroids
+    0 and 1.5)."""
+    Q = np.array([[0.0], [2.0], [1.0]])
+    var = oracle.kmeans_tie_variants(Q, 2, 1)
+    assert len(var) == 2
+    (c0, w0, ov0), (c1, w1, ov1) = var
+    assert ov0 == {} and ov1 == {(0, 2): 1}
+    np.testing.assert_array_equal(w0, [2 / 3, 1 / 3])
+    np.testing.assert_array_equal(c0[:, 0], [0.5, 2.0])
+    np.testing.assert_array_equal(w1, [1 / 3, 2 / 3])
+    np.testing.assert_array_equal(c1[:, 0], [0.0, 1.5])
+    # the plain result is kmeans_block's
+    c, w, _ = oracle.kmeans_block(Q, 2, 1)
+    np.testing.assert_array_equal(c, c0)
+    np.testing.assert_array_equal(w, w0)
+    # well-separated queries have no near-tie: one variant only
+    Qs = _video_block(3)
+    assert len(oracle.kmeans_tie_variants(Qs, 8, 4)) == 1
+
+
+def test_kmeans_tie_variants_two_ties_branch_in_order():
+    """Two exact ties in the first iteration (T = 1) give four results: the
+    plain one and each combination of the other sides."""
+    Q = np.array([[0.0], [1.0], [2.0], [1.0]])     # initial centroids q[0], q[2]
+    var = oracle.kmeans_tie_variants(Q, 2, 1)
+    assert sorted(tuple(sorted(v[2].items())) for v in var) == [
+        (), (((0, 1), 1),), (((0, 1), 1), ((0, 3), 1)), (((0, 3), 1),)]
+    counts = sorted(tuple(np.round(v[1] * 4).astype(int)) for v in var)
+    assert counts == [(1, 3), (2, 2), (2, 2), (3, 1)]
