@@ -205,6 +205,22 @@ absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k,
                                   int64_t B, int64_t H, int64_t N, int64_t d,
                                   void* hip_stream);
 
+/* absa_sparse_attention for callers that cannot allocate device memory
+ * (code under stream capture, serving loops, harnesses that forbid it):
+ * the same arguments, kernels and result, and it calls no allocator. fp32
+ * inputs are rounded to bf16 into a static scratch array that every device
+ * the library runs on holds for the life of the process (24 MiB), so they
+ * may hold at most 2^22 elements per tensor (B*H*N*d), else
+ * ABSA_ERR_UNSUPPORTED; bf16 inputs use no scratch and have no limit. All
+ * calls on one device share that scratch: fp32 calls that overlap in time
+ * on one device (on different streams) race and give unspecified outputs.
+ * Under stream capture the plan records no use, so the caller keeps the
+ * plan alive while the captured work may run. */
+absa_status absa_sparse_attention_noalloc(absa_plan plan, const void* q, const void* k,
+                                          const void* v, void* o, absa_dtype dtype,
+                                          int64_t B, int64_t H, int64_t N, int64_t d,
+                                          void* hip_stream);
+
 /* Dense softmax(Q K^T / sqrt(d)) V with the same tiles and arithmetic as
  * absa_sparse_attention (the comparator); q, k and v must be finite. */
 absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,

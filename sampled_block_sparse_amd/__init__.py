@@ -11,6 +11,7 @@ The functions carry the C names:
   absa_plan_import(rowptr, idx, logw, p, B, H, N, d) -> Plan
   absa_plan_scores(plan) -> device address of the retained scores, or 0
   absa_sparse_attention(plan, q, k, v, out=None) -> out
+  absa_sparse_attention_noalloc(plan, q, k, v, out) -> out
   absa_dense_attention(q, k, v, out=None) -> out
 Tensors are torch CUDA (HIP) tensors, contiguous [B, H, N, d], bfloat16 or
 float32; work is queued on torch's current stream unless a stream is given.
@@ -25,7 +26,7 @@ import torch
 
 __all__ = [
     "AbsaError", "Plan", "absa_plan_create", "absa_plan_from_scores", "absa_plan_import",
-    "absa_plan_scores", "absa_sparse_attention",
+    "absa_plan_scores", "absa_sparse_attention", "absa_sparse_attention_noalloc",
     "absa_dense_attention", "absa_status_string", "absa_last_error",
     "get_lib", "LIB_PATH", "ABSA_OK", "ABSA_ERR_INVALID_ARG", "ABSA_ERR_UNSUPPORTED",
     "ABSA_ERR_OUT_OF_MEMORY", "ABSA_ERR_DEVICE", "ABSA_ERR_PLAN_MISMATCH",
@@ -96,6 +97,8 @@ def get_lib():
         "absa_plan_scores": (_i32, [_vp, ctypes.POINTER(_vp)]),
         "absa_sparse_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
                                          _i64, _vp]),
+        "absa_sparse_attention_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
+                                                 _i64, _i64, _vp]),
         "absa_dense_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp]),
         "absa_plan_destroy": (None, [_vp]),
         "absa_release_cached_memory": (_i32, []),
@@ -317,6 +320,16 @@ def absa_sparse_attention(plan: Plan, q, k, v, out=None, stream=None):
     _check(get_lib().absa_sparse_attention(plan.handle, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
                                            _dev(out, "out"), _dtype_code(q), B, H, N, d,
                                            _stream(stream)))
+    return out
+
+
+def absa_sparse_attention_noalloc(plan: Plan, q, k, v, out, stream=None):
+    """The allocation-free variant: out must be given (the C call allocates
+    nothing)."""
+    B, H, N, d, out = _attention_args(q, k, v, out)
+    _check(get_lib().absa_sparse_attention_noalloc(plan.handle, _dev(q, "q"), _dev(k, "k"),
+                                                   _dev(v, "v"), _dev(out, "out"),
+                                                   _dtype_code(q), B, H, N, d, _stream(stream)))
     return out
 
 

@@ -820,6 +820,41 @@ absa_status absa_sparse_attention(absa_plan plan, const void* q, const void* k, 
     return note_use(plan, s);
 }
 
+absa_status absa_sparse_attention_noalloc(absa_plan plan, const void* q, const void* k,
+                                          const void* v, void* o, absa_dtype dtype, int64_t B,
+                                          int64_t H, int64_t N, int64_t d, void* hip_stream) {
+    if (!plan) return fail(ABSA_ERR_INVALID_ARG, "plan is NULL");
+    ABSA_TRY(attention_common(q, k, v, o, dtype, B, H, N, d));
+    if (plan->B != B || plan->H != H || plan->N != N || plan->d != d)
+        return fail(ABSA_ERR_PLAN_MISMATCH,
+                    "plan built for (B,H,N,d) = (%lld,%lld,%lld,%lld), called with (%lld,%lld,%lld,%lld)",
+                    (long long)plan->B, (long long)plan->H, (long long)plan->N, (long long)plan->d,
+                    (long long)B, (long long)H, (long long)N, (long long)d);
+    const int64_t n = B * H * N * d;
+    if (dtype == ABSA_F32 && n > kNoAllocMaxElems)
+        return fail(ABSA_ERR_UNSUPPORTED,
+                    "fp32 inputs of the allocation-free call hold at most %lld elements per tensor "
+                    "(its static scratch); got %lld",
+                    (long long)kNoAllocMaxElems, (long long)n);
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
+                   *v16 = static_cast<const uint16_t*>(v);
+    if (dtype == ABSA_F32) {
+        uint16_t* scr = nullptr;
+        ABSA_HIP(noalloc_scratch(&scr), "static scratch address");
+        uint16_t* tmp[3] = {scr, scr + kNoAllocMaxElems, scr + 2 * kNoAllocMaxElems};
+        const void* src[3] = {q, k, v};
+        for (int i = 0; i < 3; ++i)
+            ABSA_HIP(launch_to_bf16(static_cast<const float*>(src[i]), tmp[i], n, s),
+                     "fp32 to bf16 kernel");
+        q16 = tmp[0]; k16 = tmp[1]; v16 = tmp[2];
+    }
+    ABSA_HIP(launch_attention(q16, k16, v16, o, dtype == ABSA_F32, B, H, N, static_cast<int>(d),
+                              plan->rowptr, plan->idx, plan->logw, false, s),
+             "sparse attention kernel");
+    return note_use(plan, s);
+}
+
 absa_status absa_dense_attention(const void* q, const void* k, const void* v, void* o,
                                  absa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
                                  void* hip_stream) {

@@ -70,6 +70,12 @@ hipError_t launch_sip_fill(const float* scores, int64_t rows, int64_t M,
                            const int64_t* rowptr, int sampling, int32_t* idx, float* logw,
                            double* p, hipStream_t s);
 
+// Static scratch of the allocation-free attention call: three bf16 copies of
+// fp32 inputs of at most kNoAllocMaxElems elements each. noalloc_scratch
+// gives its address on the current device (looked up once per device).
+constexpr int64_t kNoAllocMaxElems = int64_t(1) << 22;
+hipError_t noalloc_scratch(uint16_t** out);
+
 // fp32 -> bf16 (round to nearest even) of n elements, n a multiple of 8.
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 

@@ -56,7 +56,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 namespace absa {
 namespace {
@@ -570,7 +572,34 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ 
     }
 }
 
+// Scratch of the allocation-free attention call (bf16 copies of fp32 q, k,
+// v): one copy of this array lives on every device the library runs on, for
+// the life of the process. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it passes the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint16_t scratch[3 * kNoAllocMaxElems];
+
+std::mutex g_scratch_mutex;
+std::vector<uint16_t*> g_scratch_addr;   // per device, null until looked up
+
 }  // namespace
+
+hipError_t noalloc_scratch(uint16_t** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (static_cast<size_t>(dev) >= g_scratch_addr.size()) g_scratch_addr.resize(dev + 1, nullptr);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = static_cast<uint16_t*>(p);
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
     const int64_t n8 = n / 8;                   // n is a multiple of 8 (d in {64, 128})

@@ -26,7 +26,7 @@ def test_header_declares_the_interface():
                      "absa_plan_info", "absa_plan_export", "absa_plan_export_intermediate",
                      "absa_sparse_attention", "absa_dense_attention", "absa_plan_destroy",
                      "absa_status_string", "absa_last_error", "absa_plan_params_init",
-                     "absa_plan_scores"):
+                     "absa_plan_scores", "absa_sparse_attention_noalloc"):
         assert required in names
 
 
@@ -140,6 +140,8 @@ def test_other_calls_reject_before_device_work():
     assert lib.absa_plan_export_intermediate(None, 0, 0, 0, None) == absa.ABSA_ERR_INVALID_ARG
     ptr = ctypes.c_void_p(7)
     assert lib.absa_plan_scores(None, ctypes.byref(ptr)) == absa.ABSA_ERR_INVALID_ARG
+    assert lib.absa_sparse_attention_noalloc(None, _FAKE, _FAKE, _FAKE, _FAKE, 0, 1, 1, 1024, 64,
+                                             None) == absa.ABSA_ERR_INVALID_ARG
     lib.absa_plan_destroy(None)     # no-op
 
 
