@@ -30,7 +30,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "CONFIGS", "budget_blocks", "iid_qkv", "video_qkv", "drift", "make_inputs",
+    "CONFIGS", "budget_blocks", "iid_qkv", "video_qkv", "drift", "drift_device", "make_inputs",
     "sip_seed", "shape_of",
 ]
 
@@ -130,6 +130,16 @@ def drift(x: torch.Tensor, seed: int, sigma: float = REUSE_SIGMA) -> torch.Tenso
     rng = np.random.Generator(np.random.PCG64(seed))
     z = rng.standard_normal(tuple(x.shape), dtype=np.float32)
     return (x.float() + torch.from_numpy(z) * sigma).to(x.dtype)
+
+
+def drift_device(x: torch.Tensor, seed: int, sigma: float = REUSE_SIGMA) -> torch.Tensor:
+    """drift() drawn on x's device with torch's generator for that device
+    (seeded; a different stream of numbers than drift(), for the bench's
+    full-size multi-step runs, where drawing on the host would dominate)."""
+    g = torch.Generator(device=x.device)
+    g.manual_seed(seed)
+    z = torch.randn(tuple(x.shape), generator=g, device=x.device, dtype=torch.float32)
+    return (x.float() + z * sigma).to(x.dtype)
 
 
 def make_inputs(name: str, threads: int = 8):

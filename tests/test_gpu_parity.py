@@ -561,3 +561,35 @@ def test_destroy_is_stream_ordered():
             assert torch.equal(o, ref), f"rep {rep}"
         for j in junk:
             j.destroy()
+
+
+def test_multi_step_schedule_against_oracle():
+    """The pages' schedule in small [hamidun, kernel paragraph and "how it was
+    measured": full attention in the first steps, then the sparse kernel
+    with a plan rebuilt every 4 steps]: 2 dense steps, then 8 sparse steps
+    with plans built at sparse steps 0 and 4, Q/K/V drifting by 0.05 N(0,1)
+    every step. Every step's output is checked against the oracle on that
+    step's inputs (dense attention, or HT attention under the plan in use),
+    on three of the heads."""
+    q, k, v = synth.make_inputs("small")
+    B, H, N, d = q.shape
+    budget = synth.budget_blocks(10, N // 4)
+    hs = [0, H // 2, H - 1]
+    plan = gp = None
+    for step in range(10):
+        if step:
+            q, k, v = (synth.drift(x, seed=500 + 10 * step + i) for i, x in enumerate((q, k, v)))
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        Q, K, V = to64(q)[:, hs], to64(k)[:, hs], to64(v)[:, hs]
+        if step < 2:
+            out = absa.absa_dense_attention(qd, kd, vd)
+            torch.cuda.synchronize()
+            check_output(to64(out)[:, hs], oracle.dense_attention(Q, K, V), f"dense step {step}")
+            continue
+        if (step - 2) % 4 == 0:
+            plan = absa.absa_plan_create(qd, kd, budget, synth.sip_seed(step))
+            gp = plan.export()
+        out = absa.absa_sparse_attention(plan, qd, kd, vd)
+        torch.cuda.synchronize()
+        sub = oracle.OraclePlan(B, len(hs), N, d, N // 4, (N + 127) // 128, *_subplan(gp, H, hs, N))
+        check_output(to64(out)[:, hs], oracle.plan_attention(Q, K, V, sub), f"sparse step {step}")
