@@ -55,7 +55,18 @@
 extern "C" {
 #endif
 
-typedef enum absa_status {
+/* The enums below cross the ABI as 32-bit integers. A C caller may pass any
+ * int, so in C++ they carry a fixed underlying type: every int32 value is then
+ * a valid value of the type, and an out-of-range one reaches the argument
+ * checks (ABSA_ERR_UNSUPPORTED / ABSA_ERR_INVALID_ARG) instead of being
+ * undefined behaviour. */
+#ifdef __cplusplus
+#define ABSA_ENUM_BASE : int32_t
+#else
+#define ABSA_ENUM_BASE
+#endif
+
+typedef enum absa_status ABSA_ENUM_BASE {
     ABSA_OK = 0,
     ABSA_ERR_INVALID_ARG = 1,   /* null pointer, value out of range, bad scores */
     ABSA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement  */
@@ -64,7 +75,7 @@ typedef enum absa_status {
     ABSA_ERR_PLAN_MISMATCH = 5  /* plan built for another (B, H, N, d)          */
 } absa_status;
 
-typedef enum absa_dtype {
+typedef enum absa_dtype ABSA_ENUM_BASE {
     ABSA_BF16 = 0,              /* bfloat16 storage; MFMA inputs as stored         */
     ABSA_F32 = 1                /* float32 storage; rounded to bf16 for the MFMA   */
 } absa_dtype;
@@ -83,7 +94,7 @@ typedef struct absa_plan_s* absa_plan;
  *               rounding left the fixed-point total off K 2^40), each block
  *               is taken with probability P 2^-40 exactly, and that is the
  *               p the plan records and weights by. */
-typedef enum absa_sampling {
+typedef enum absa_sampling ABSA_ENUM_BASE {
     ABSA_SAMPLING_POISSON = 0,
     ABSA_SAMPLING_SYSTEMATIC = 1
 } absa_sampling;
@@ -113,7 +124,7 @@ typedef struct absa_plan_params {
 } absa_plan_params;
 
 /* Which retained intermediate absa_plan_export_intermediate copies. */
-typedef enum absa_intermediate {
+typedef enum absa_intermediate ABSA_ENUM_BASE {
     ABSA_INTER_MEAN_KEYS = 0,   /* float [B, H, M, d], M = N/4                   */
     ABSA_INTER_CENTROIDS = 1,   /* float [B, H, QB, C, d], QB = ceil(N/128)       */
     ABSA_INTER_WEIGHTS = 2,     /* float [B, H, QB, C]                            */
