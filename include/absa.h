@@ -111,7 +111,13 @@ typedef enum absa_sampling ABSA_ENUM_BASE {
  * value (default POISSON). keep_intermediates != 0 keeps
  * the mean keys, centroids, weights and scores on the device for
  * absa_plan_export_intermediate; otherwise they are freed when the plan is
- * built. */
+ * built. fused != 0 builds the plan with the second score pass and the SIP
+ * count in one kernel [hamidun, IBCS paragraph into the SIP paragraph]: a
+ * workgroup computes the scores of two query blocks into on-chip memory and
+ * runs their water-filling and draws from there, so no score row goes
+ * through device memory. The plan is bit-identical to the default path's.
+ * It needs n_clusters <= 8, M = N/4 <= 20224 and keep_intermediates = 0
+ * (ABSA_ERR_UNSUPPORTED otherwise). */
 typedef struct absa_plan_params {
     int32_t query_block;
     int32_t kv_block;
@@ -121,6 +127,7 @@ typedef struct absa_plan_params {
     uint64_t seed;
     int32_t keep_intermediates;
     int32_t sampling;           /* absa_sampling */
+    int32_t fused;              /* 0: two score passes, then SIP; else fused */
 } absa_plan_params;
 
 /* Which retained intermediate absa_plan_export_intermediate copies. */
@@ -132,7 +139,7 @@ typedef enum absa_intermediate ABSA_ENUM_BASE {
 } absa_intermediate;
 
 /* Fill *out with the defaults: 128, 4, 8 clusters, 4 iterations, budget 1,
- * seed 0, keep_intermediates 0, POISSON sampling. Returns
+ * seed 0, keep_intermediates 0, POISSON sampling, fused 0. Returns
  * ABSA_ERR_INVALID_ARG on NULL. */
 absa_status absa_plan_params_init(absa_plan_params* out);
 

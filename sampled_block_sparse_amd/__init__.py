@@ -47,7 +47,7 @@ _i64, _u64, _i32, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.
 class _Params(ctypes.Structure):
     _fields_ = [("query_block", _i32), ("kv_block", _i32), ("n_clusters", _i32),
                 ("kmeans_iters", _i32), ("budget_blocks", _i64), ("seed", _u64),
-                ("keep_intermediates", _i32), ("sampling", _i32)]
+                ("keep_intermediates", _i32), ("sampling", _i32), ("fused", _i32)]
 
 
 # absa_sampling
@@ -229,7 +229,8 @@ class Plan:
 
 def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed: int,
                      n_clusters: int = 8, kmeans_iters: int = 4,
-                     keep_intermediates: bool = False, sampling="poisson", stream=None) -> Plan:
+                     keep_intermediates: bool = False, sampling="poisson", fused: bool = False,
+                     stream=None) -> Plan:
     B, H, N, d = _shape4(q)
     if tuple(k.shape) != (B, H, N, d) or k.dtype != q.dtype:
         raise ValueError("q and k must share shape and dtype")
@@ -242,6 +243,7 @@ def absa_plan_create(q: torch.Tensor, k: torch.Tensor, budget_blocks: int, seed:
     prm.seed = seed & 0xFFFFFFFFFFFFFFFF
     prm.keep_intermediates = 1 if keep_intermediates else 0
     prm.sampling = _sampling_code(sampling)
+    prm.fused = 1 if fused else 0
     out = _vp()
     _check(lib.absa_plan_create(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, N, d,
                                 ctypes.byref(prm), _stream(stream), ctypes.byref(out)))

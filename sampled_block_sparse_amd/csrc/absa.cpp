@@ -310,6 +310,7 @@ class WorkspaceLease {
 struct PlanTemps {
     float* kbar = nullptr;
     int8_t* kq = nullptr;
+    int8_t* kqt = nullptr;       // tile-major digits (fused plans only)
     int* kx = nullptr;
     float* cent = nullptr;
     float* w = nullptr;
@@ -378,15 +379,26 @@ absa_status sip_temps(A& a, const absa_plan_s* P, PlanTemps& t) {
 // rowptr/idx/logw/p of the plan (allocated in arena, owned by the plan)
 // using the temporaries in t. One device-to-host read of the total count and
 // the score check flag, then the fill kernel. Returns with the fill queued;
-// the caller synchronises.
+// the caller synchronises. With fused set (plan_create only, scores =
+// t.scores), the scores come from the fused pass-2 + SIP kernel on t's
+// centroids, weights, key digits and pass-1 statistics, which writes into
+// t.scores only what the fill kernel reads.
 absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_t seed,
-                    int sampling, hipStream_t s, DeviceArena& arena, const PlanTemps& t) {
+                    int sampling, hipStream_t s, DeviceArena& arena, const PlanTemps& t,
+                    bool fused = false) {
     const int64_t rows = P->rows;
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
     ABSA_HIP(hipMemsetAsync(t.status, 0, sizeof(PlanStatus), s), "clear plan status");
-    ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, sampling,
-                              t.capmask, t.keepmask, t.rowinfo, t.counts, t.status, s),
-             "SIP count kernel");
+    if (fused)
+        ABSA_HIP(launch_scores_sip(t.cent, t.w, t.kqt, t.kx, t.part, P->B, P->H, P->QB, P->M,
+                                   static_cast<int>(P->d), P->n_clusters, budget, seed, sampling,
+                                   t.scores, t.capmask, t.keepmask, t.rowinfo, t.counts, t.status,
+                                   s),
+                 "fused score and SIP kernel");
+    else
+        ABSA_HIP(launch_sip_count(scores, P->B, P->H, P->QB, P->M, budget, seed, sampling,
+                                  t.capmask, t.keepmask, t.rowinfo, t.counts, t.status, s),
+                 "SIP count kernel");
     ABSA_HIP(launch_scan(t.counts, rows, P->rowptr, t.status, s), "row scan kernel");
     PlanStatus host{};
     ABSA_HIP(hipMemcpyAsync(&host, t.status, sizeof(PlanStatus), hipMemcpyDeviceToHost, s),
@@ -504,6 +516,7 @@ absa_status absa_plan_params_init(absa_plan_params* out) {
     out->seed = 0;
     out->keep_intermediates = 0;
     out->sampling = ABSA_SAMPLING_POISSON;
+    out->fused = 0;
     return ABSA_OK;
 }
 
@@ -530,6 +543,12 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     if (params->budget_blocks < 1 || params->budget_blocks > M)
         return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
                     (long long)M, (long long)params->budget_blocks);
+    const bool fused = params->fused != 0;
+    if (fused && (params->n_clusters > 8 || M > kFusedMaxBlocks || params->keep_intermediates))
+        return fail(ABSA_ERR_UNSUPPORTED,
+                    "fused needs n_clusters <= 8 (got %d), M <= %lld (got %lld) and "
+                    "keep_intermediates = 0",
+                    params->n_clusters, (long long)kFusedMaxBlocks, (long long)M);
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     absa_plan_s* P = new (std::nothrow) absa_plan_s();
@@ -553,6 +572,9 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
                 ABSA_TRY(a.alloc(&t.scores, P->rows * M, "scores"));
             }
             ABSA_TRY(a.alloc(&t.kq, B * H * M * 3 * d, "mean-key digits"));
+            if (fused)
+                ABSA_TRY(a.alloc(&t.kqt, kqt_bytes(B * H, M, static_cast<int>(d)),
+                                 "tile-major mean-key digits"));
             ABSA_TRY(a.alloc(&t.kx, B * H * M, "mean-key exponents"));
             ABSA_TRY(a.alloc(&t.part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
             return sip_temps(a, P, t);
@@ -577,17 +599,18 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
         SideFork fork(s);
         hipStream_t side = nullptr;
         ABSA_TRY(fork.fork(&side));
-        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kq, t.kx, side),
+        ABSA_HIP(launch_mean_keys(k, dt, B * H, N, static_cast<int>(d), t.kbar, t.kq, t.kqt, t.kx,
+                                  side),
                  "mean-key kernel");
         ABSA_HIP(launch_kmeans(q, dt, B * H, N, static_cast<int>(d), C, params->kmeans_iters,
                                t.cent, t.w, s),
                  "k-means kernel");
         ABSA_TRY(fork.join());
         ABSA_HIP(launch_scores(t.cent, t.w, t.kq, t.kx, B * H, P->QB, M, static_cast<int>(d), C,
-                               t.part, t.scores, s),
+                               t.part, t.scores, !fused, s),
                  "score kernel");
         ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, params->sampling, s,
-                         arena, t));
+                         arena, t, fused));
         keep(arena, P);
         // the workspace is released (and may be reused) only once the build
         // has finished on the device

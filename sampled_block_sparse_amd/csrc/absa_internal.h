@@ -40,9 +40,12 @@ struct PlanStatus {
 
 // kbar: fp32 means [BH, M, d], or null to skip them; kq: their block floating point int8 digits
 // [BH, M, 3, d] (planes X2, X1, X0) and kx: the exponent of each mean [BH, M],
-// the score kernel's operand.
+// the score kernel's operand; kqt, or null to skip it: the same digits
+// tile-major for the fused score kernel ([BH, ceil(M/16), 3, d/64, 64 lanes,
+// 16 bytes]: kqt_bytes).
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, int8_t* kq, int* kx, hipStream_t s);
+                            float* kbar, int8_t* kq, int8_t* kqt, int* kx, hipStream_t s);
+inline int64_t kqt_bytes(int64_t BH, int64_t M, int d) { return BH * ((M + 15) / 16) * 16 * 3 * d; }
 
 hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
                          int C, int iters, float* cent, float* w, hipStream_t s);
@@ -51,9 +54,25 @@ hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
 // argument of launch_scores).
 int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C);
 
+// Both score passes, or (pass2 = false) pass 1 alone, whose chunk
+// statistics launch_scores_sip takes.
 hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
                          int64_t BH, int64_t QB, int64_t M, int d, int C,
-                         float2* part, float* scores, hipStream_t s);
+                         float2* part, float* scores, bool pass2, hipStream_t s);
+
+// Score pass 2 fused with the SIP count: the same outputs as pass 2 and
+// launch_sip_count, except that scores receives only the scores the fill
+// kernel reads (kept blocks that are not capped). Needs C <= 8 and
+// M <= kFusedMaxBlocks; part from launch_scores(..., pass2 = false), kqt
+// from launch_mean_keys.
+constexpr int kFusedThreads = 1024;
+constexpr int64_t kFusedMaxBlocks = 20224;
+hipError_t launch_scores_sip(const float* cent, const float* w, const int8_t* kqt, const int* kx,
+                             const float2* part, int64_t B, int64_t H, int64_t QB, int64_t M,
+                             int d, int C, int64_t budget, uint64_t seed, int sampling,
+                             float* scores, uint64_t* capmask, uint64_t* keepmask,
+                             SipRow* rowinfo, int64_t* counts, PlanStatus* status,
+                             hipStream_t s);
 
 hipError_t launch_sip_count(const float* scores, int64_t B, int64_t H, int64_t QB,
                             int64_t M, int64_t budget, uint64_t seed, int sampling,

@@ -65,8 +65,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
                                                         float* __restrict__ kbar,
                                                         int8_t* __restrict__ kq,
+                                                        int8_t* __restrict__ kqt,
                                                         int* __restrict__ kx, int64_t chunks,
-                                                        int d) {
+                                                        int64_t M, int d) {
     const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const bool ok = c < chunks;
     const int per_row = d >> 2;                 // 16 or 32 lanes per KV block
@@ -90,13 +91,29 @@ __global__ __launch_bounds__(256) void mean_keys_kernel(const T* __restrict__ k,
     int8_t pl[3][4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) bfp_digits(acc[e], ex, pl[0][e], pl[1][e], pl[2][e]);
-    int8_t* dst = kq + blk * 3 * d + d0;
+    uint32_t word[3];
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<uint32_t*>(dst + q * d) =
-            static_cast<uint8_t>(pl[q][0]) | (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][1])) << 8) |
-            (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][2])) << 16) |
-            (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][3])) << 24);
+        word[q] = static_cast<uint8_t>(pl[q][0]) | (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][1])) << 8) |
+                  (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][2])) << 16) |
+                  (static_cast<uint32_t>(static_cast<uint8_t>(pl[q][3])) << 24);
+    int8_t* dst = kq + blk * 3 * d + d0;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<uint32_t*>(dst + q * d) = word[q];
+    if (kqt) {
+        // The same digits tile-major, for the fused score kernel's B operands:
+        // 16-key tile T, plane q, 64-channel step st form one 1 KB run in
+        // MFMA lane order (lane 16 g + j % 16 holds channels 64 st + 16 g ..
+        // +16 of key j), so that each operand load reads 1 KB contiguously.
+        const int64_t bh = blk / M, j = blk - bh * M;
+        const int64_t ntile = (M + 15) / 16;
+        const int nstep = d >> 6;
+        const int st = d0 >> 6, g = (d0 & 63) >> 4;
+        int8_t* tdst = kqt + ((bh * ntile + j / 16) * 3 * nstep + st) * 1024 + g * 256 +
+                       (j % 16) * 16 + (d0 & 15);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *reinterpret_cast<uint32_t*>(tdst + q * nstep * 1024) = word[q];
+    }
     if (d0 == 0) kx[blk] = ex;
 }
 
@@ -400,6 +417,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTile = 32;
+
+// Pass 2's exponent bias of centroid m of query block r: the centroid's
+// chunk statistics (reference, sum) combined in chunk order into its
+// softmax denominator Z (relative to the largest reference R), folded with
+// the centroid's weight: w_m 2^(x - R) / Z = 2^(x + log2(w_m / Z) - R).
+// -inf for a slot past QB or C, or of weight 0.
+__device__ __forceinline__ float score_bias(const float2* __restrict__ part,
+                                            const float* __restrict__ w, int64_t bh, int64_t QB,
+                                            int C, int nchunks, int64_t r, int m) {
+    if (r >= QB || m >= C) return -INFINITY;
+    const float2* pp = part + ((bh * QB + r) * C + m) * nchunks;
+    float mx = -INFINITY;
+    for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, pp[c].x);
+    float z = 0.0f;
+    for (int c = 0; c < nchunks; ++c) {
+        const float2 q = pp[c];
+        if (q.x != -INFINITY) z += q.y * __builtin_amdgcn_exp2f(q.x - mx);
+    }
+    const float wm = w[(bh * QB + r) * C + m];
+    return (wm > 0.0f) ? log2f(wm / z) - mx : -INFINITY;
+}
 
 // The score contraction of one head runs in two passes over key chunks, so
 // the grid has (query-block groups) x (heads) x (chunks) workgroups and
@@ -750,19 +788,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int slot = slot_of(i);
-            bias[i] = -INFINITY;
-            if (slot_valid(slot)) {
-                const float2* pp = part + part_index(slot);
-                float m = -INFINITY;
-                for (int c = 0; c < nchunks; ++c) m = fmaxf(m, pp[c].x);
-                float z = 0.0f;
-                for (int c = 0; c < nchunks; ++c) {
-                    const float2 q = pp[c];
-                    if (q.x != -INFINITY) z += q.y * __builtin_amdgcn_exp2f(q.x - m);
-                }
-                const float wm = w[(bh * QB + r0 + slot / CP) * C + slot % CP];
-                if (wm > 0.0f) bias[i] = log2f(wm / z) - m;
-            }
+            bias[i] = score_bias(part, w, bh, QB, C, nchunks, r0 + slot / CP, slot % CP);
         }
         float pr[RPW];
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
@@ -1046,18 +1072,25 @@ __device__ __forceinline__ float fp32_at_least(double x) {
 // latency of the rounds' reductions than the spill costs (2.42 against
 // 2.65 ms on 40 x 591 rows of 18,900 blocks); at 32 pairs the scores alone
 // fill most of the 80 registers, and that tier keeps two workgroups.
-template <int NT, int MAXP>
-__global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_count_kernel(
-    const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
-    uint64_t seed, int sampling, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
-    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+//
+// sip_row is the work of one row, for a workgroup of NT threads: load_pair(i)
+// gives the scores of blocks 2i and 2i+1 (-1 past M: never capped, never
+// kept), and on_kept(j, s_j) is called for every kept block j whose p
+// depends on its score (not capped, mode 2): the blocks whose score the fill
+// kernel reads. redd and redi hold 32 reduction slots ([16, 32): rounds 0,
+// 2, ...; [0, 16): block_sum, rounds 1, 3, ...), redu NT/64.
+template <int NT, int MAXP, typename LoadPair, typename OnKept>
+__device__ __forceinline__ void sip_row(int64_t row, LoadPair&& load_pair, OnKept&& on_kept,
+                                        int64_t H, int64_t QB, int64_t M, int64_t budget,
+                                        uint64_t seed, int sampling,
+                                        uint64_t* __restrict__ capmask,
+                                        uint64_t* __restrict__ keepmask,
+                                        SipRow* __restrict__ rowinfo,
+                                        int64_t* __restrict__ counts,
+                                        PlanStatus* __restrict__ status, double* redd, int* redi,
+                                        uint64_t* redu) {
     constexpr int kSipPairsPerPass = NT;                 // block pairs per pass
     static_assert(NT / 64 <= 16, "reduction slots");
-    __shared__ double redd[32];        // [16, 32): rounds 0, 2, ...; [0, 16): block_sum, rounds 1, 3, ...
-    __shared__ int redi[32];
-    __shared__ uint64_t redu[NT / 64];
-    const int64_t row = blockIdx.x;
-    const float* sg = scores + row * M;
     const int64_t words = (M + 63) / 64;
     uint64_t* km = keepmask + row * words;
     uint64_t* cm = capmask + row * words;
@@ -1067,11 +1100,6 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
     const int M32 = static_cast<int>(M);                  // M < 2^19
     const int npairs = (M32 + 1) / 2;
     const int npass = (npairs + kSipPairsPerPass - 1) / kSipPairsPerPass;
-    // Scores of pair i (blocks past M read as -1: never capped, never kept).
-    auto load_pair = [&](int i) {
-        const int j = 2 * i;
-        return make_float2(j < M32 ? sg[j] : -1.0f, j + 1 < M32 ? sg[j + 1] : -1.0f);
-    };
     // register copies of the thread's pairs (two plain arrays so that they
     // stay in registers)
     // (at most 32 floats each: longer arrays the compiler leaves in scratch
@@ -1256,6 +1284,10 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
             const bool cap0 = v.x >= thr_min, cap1 = v.y >= thr_min;
             const bool keep0 = 2 * i < M32 && u0 < sip_p(cap0, ri, v.x);
             const bool keep1 = 2 * i + 1 < M32 && u1 < sip_p(cap1, ri, v.y);
+            if (ri.mode == 2) {
+                if (keep0 && !cap0) on_kept(2 * i, v.x);
+                if (keep1 && !cap1) on_kept(2 * i + 1, v.y);
+            }
             emit(k, keep0, keep1, cap0, cap1);
         };
         if constexpr (MAXP > 0) {
@@ -1284,11 +1316,17 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
             return z;
         };
         // pass k given the prefix before the pair of lane 0 (wave-uniform)
-        auto take = [&](int k, const PairSizes& z, uint64_t before, uint64_t incl) {
+        auto take = [&](int k, float2 v, const PairSizes& z, uint64_t before, uint64_t incl) {
             const uint64_t c_prev = before + incl - (z.p0 + z.p1);
             const uint64_t c0 = c_prev + z.p0, c1 = c0 + z.p1;
             const uint64_t n_prev = sys_points_below(c_prev, U), n0 = sys_points_below(c0, U);
-            emit(k, n0 > n_prev, sys_points_below(c1, U) > n0, z.cap0, z.cap1);
+            const bool keep0 = n0 > n_prev, keep1 = sys_points_below(c1, U) > n0;
+            if (ri.mode == 2) {
+                const int i = ibase_d + kPassStep * k;
+                if (keep0 && !z.cap0) on_kept(2 * i, v.x);
+                if (keep1 && !z.cap1) on_kept(2 * i + 1, v.y);
+            }
+            emit(k, keep0, keep1, z.cap0, z.cap1);
         };
         if constexpr (MAXP > 0) {
             // the wave's range is contiguous: its prefix is the earlier
@@ -1309,9 +1347,10 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
 #pragma unroll
             for (int k = 0; k < MAXP; ++k) {
                 if (in_row_d(k)) {
-                    const PairSizes z = sizes(k, get_pair(k));
+                    const float2 v = get_pair(k);
+                    const PairSizes z = sizes(k, v);
                     const uint64_t incl = wave_scan_u64(z.p0 + z.p1);
-                    take(k, z, before, incl);
+                    take(k, v, z, before, incl);
                     before += wave_last_u64(incl);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -1320,7 +1359,8 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
             // pass k covers pairs NT k .. NT k + NT - 1 across the waves
             uint64_t run = 0;
             for (int k = 0; k < npass; ++k) {
-                const PairSizes z = sizes(k, pair_at(k));
+                const float2 v = pair_at(k);
+                const PairSizes z = sizes(k, v);
                 const uint64_t incl = wave_scan_u64(z.p0 + z.p1);
                 if (lane == 63) redu[wave] = incl;
                 __syncthreads();
@@ -1330,7 +1370,7 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
                     if (w2 < wave) before += t;
                     tot += t;
                 }
-                take(k, z, before, incl);
+                take(k, v, z, before, incl);
                 run += tot;
                 __syncthreads();
             }
@@ -1340,6 +1380,220 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
     if (tid == 0) {
         counts[row] = tk;
         rowinfo[row] = ri;
+    }
+}
+
+// The SIP count of plan row blockIdx.x from its scores in global memory.
+template <int NT, int MAXP>
+__global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_count_kernel(
+    const float* __restrict__ scores, int64_t H, int64_t QB, int64_t M, int64_t budget,
+    uint64_t seed, int sampling, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
+    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    __shared__ double redd[32];
+    __shared__ int redi[32];
+    __shared__ uint64_t redu[NT / 64];
+    const int64_t row = blockIdx.x;
+    const float* sg = scores + row * M;
+    const int M32 = static_cast<int>(M);                  // M < 2^19
+    auto load_pair = [&](int i) {
+        const int j = 2 * i;
+        return make_float2(j < M32 ? sg[j] : -1.0f, j + 1 < M32 ? sg[j + 1] : -1.0f);
+    };
+    sip_row<NT, MAXP>(row, load_pair, [](int, float) {}, H, QB, M, budget, seed, sampling,
+                      capmask, keepmask, rowinfo, counts, status, redd, redi, redu);
+}
+
+// ---------------------------------------------------------------------------
+// Score pass 2 and the SIP count fused [hamidun, IBCS and SIP paragraphs]:
+// the scores of a query block go from the matrix products straight to its
+// water-filling and draws, without a round trip through memory. One
+// workgroup of kFusedThreads threads per pair of query blocks (r, r+1) of a
+// head, for plans of at most 8 clusters and rows of at most kFusedMaxBlocks
+// KV blocks: the pair's two score rows sit in LDS (at most 158 KB).
+//
+// The scores are the two-pass kernel's bit for bit: the same block floating
+// point digits (the centroid exponent is taken over the same group of
+// 32 / CP query blocks, CP the two-pass kernel's cluster slots per query
+// block), the same exact int32 digit products, the same fp32 combination,
+// bias (from pass 1's chunk statistics) and order of the sum over clusters.
+// The contraction runs on the 16x16x64 int8 MFMA: A = the pair's 16
+// centroid slots (query block r + s/8, cluster s%8), B = 16 keys; D layout:
+// lane l holds key l%16 and slots 4 (l/16) + i, i < 4, i.e. the four
+// clusters of one half of the query block's clusters, whose partial sum the
+// lane sixteen apart completes. Each wave takes every 16th 16-key tile, so
+// the workgroup reads its head's key digits front to back once; the tile's
+// digits (the tile-major copy the mean-key kernel writes, one contiguous
+// 1 KB run per operand load) go straight to registers (no LDS: the rows
+// fill it), two tiles alternating so that one loads while the other is
+// computed.
+//
+// Then each row's SIP count (sip_row) runs on all the workgroup's waves
+// with the scores read from LDS; the only scores written to memory are
+// those of kept blocks whose p depends on them, at their positions in the
+// row (the fill kernel reads no others).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
+    const float* __restrict__ cent, const float* __restrict__ w, const int8_t* __restrict__ kqt,
+    const int* __restrict__ kx, const float2* __restrict__ part, int64_t H, int64_t QB, int64_t M,
+    int C, int nchunks, float scale_log2, int64_t budget, uint64_t seed, int sampling,
+    float* __restrict__ scores, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
+    SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
+    constexpr int NT = kFusedThreads;
+    constexpr int NSTEP = D / 64;                   // MFMA k-steps (64 channels each)
+    constexpr int NW = NT / 64;
+    typedef int intx4 __attribute__((ext_vector_type(4)));
+    __shared__ float srow[2][kFusedMaxBlocks];
+    __shared__ double redd[32];
+    __shared__ int redi[32];
+    __shared__ uint64_t redu[NW];
+    __shared__ float wmax[NW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.y;
+    const int64_t r = 2 * static_cast<int64_t>(blockIdx.x);
+    const int M32 = static_cast<int>(M);
+
+    // Exponent of the centroids: the largest |c| over the query blocks of
+    // the two-pass kernel's wave group (32 / CP of them, aligned; an even r
+    // and its successor lie in the same group) and their C clusters.
+    const int cp = C <= 1 ? 1 : C <= 2 ? 2 : C <= 4 ? 4 : 8;
+    const int64_t grp = 32 / cp;
+    const int64_t g0 = (r / grp) * grp;
+    const int64_t gn = ((g0 + grp < QB) ? grp : QB - g0) * C * D;
+    float amax = 0.0f;
+    {
+        // gn is a multiple of D, the rows 256-byte aligned: float4 reads
+        const float4* gsrc = reinterpret_cast<const float4*>(cent + (bh * QB + g0) * C * D);
+        for (int64_t e = tid; e < gn / 4; e += NT) {
+            const float4 x = gsrc[e];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (lane == 0) wmax[wave] = amax;
+        __syncthreads();
+        amax = wmax[0];
+        for (int k = 1; k < NW; ++k) amax = fmaxf(amax, wmax[k]);
+    }
+    const int ex = bfp_exponent(amax);
+    const float rowf = ldexpf(scale_log2, ex - 28);
+
+    // A operands: slot s = lane % 16, channels 64 st + 16 (lane / 16) .. +16.
+    intx4 a2[NSTEP], a1[NSTEP], a0[NSTEP];
+    {
+        const int slot = lane & 15;
+        const int64_t rs = r + (slot >> 3);
+        const int m = slot & 7;
+        const bool ok = rs < QB && m < C;
+        // an empty slot reads centroid 0 of block r (in bounds) and uses zeros:
+        // unconditional vector loads, all in flight together
+        const float4* src = reinterpret_cast<const float4*>(
+            cent + ((bh * QB + (ok ? rs : r)) * C + (ok ? m : 0)) * D + (lane >> 4) * 16);
+        float4 xv[NSTEP][4];
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xv[st][u] = src[st * 16 + u];
+        }
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            int8_t h2[16], h1[16], h0[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float4 x4 = xv[st][e >> 2];
+                const float x = (e & 3) == 0 ? x4.x : (e & 3) == 1 ? x4.y : (e & 3) == 2 ? x4.z : x4.w;
+                bfp_digits(ok ? x : 0.0f, ex, h2[e], h1[e], h0[e]);
+            }
+            __builtin_memcpy(&a2[st], h2, 16);
+            __builtin_memcpy(&a1[st], h1, 16);
+            __builtin_memcpy(&a0[st], h0, 16);
+        }
+    }
+    // this lane's output slots 4 (lane / 16) + i: query block r + lane / 32,
+    // clusters 4 ((lane / 16) % 2) + i
+    float bias[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        bias[i] = score_bias(part, w, bh, QB, C, nchunks, r + (lane >> 5), 4 * ((lane >> 4) & 1) + i);
+
+    const int ntile = (M32 + 15) / 16;
+    const int8_t* kt = kqt + bh * ntile * (3 * D * 16) + lane * 16;
+    const int* kxb = kx + bh * M;
+    const int kc = lane & 15;
+    const bool writer = ((lane >> 4) & 1) == 0;
+    float* sr = srow[lane >> 5];
+    // digits of this lane's key of tile t (tile-major digits: each operand a
+    // contiguous 1 KB run; tiles past the row re-read the last tile, keys
+    // past M are never stored)
+    struct Tile { intx4 b2[NSTEP], b1[NSTEP], b0[NSTEP]; int kexp; };
+    auto fetch = [&](int t, Tile& tl) __attribute__((always_inline)) {
+        const int tc = min(t, ntile - 1);
+        const int8_t* kp = kt + static_cast<int64_t>(tc) * (3 * D * 16);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            tl.b2[st] = *reinterpret_cast<const intx4*>(kp + st * 1024);
+            tl.b1[st] = *reinterpret_cast<const intx4*>(kp + (NSTEP + st) * 1024);
+            tl.b0[st] = *reinterpret_cast<const intx4*>(kp + (2 * NSTEP + st) * 1024);
+        }
+        tl.kexp = kxb[min(tc * 16 + kc, M32 - 1)];
+    };
+    auto compute = [&](int t, const Tile& tl) __attribute__((always_inline)) {
+        intx4 o22 = intx4{}, o21 = intx4{}, o20 = intx4{};
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            o22 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2[st], tl.b2[st], o22, 0, 0, 0);
+            o21 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2[st], tl.b1[st], o21, 0, 0, 0);
+            o20 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2[st], tl.b0[st], o20, 0, 0, 0);
+            o21 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], tl.b2[st], o21, 0, 0, 0);
+            o20 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], tl.b1[st], o20, 0, 0, 0);
+            o20 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[st], tl.b2[st], o20, 0, 0, 0);
+        }
+        // the two-pass kernel's combination and key factor, then its sum over
+        // the half's clusters in cluster order, then the two halves
+        const float cf = ldexpf(rowf, tl.kexp);
+        float pr = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lo = (o21[i] << 8) + o20[i];
+            const float x = fmaf(static_cast<float>(o22[i]), 65536.0f, static_cast<float>(lo));
+            pr += __builtin_amdgcn_exp2f(fmaf(x, cf, bias[i]));
+        }
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_int(pr), __float_as_int(pr),
+                                                          false, false);
+        const float sc = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        const int j = t * 16 + kc;
+        if (writer && j < M32) sr[j] = sc;
+    };
+    // two tiles in registers, alternately loaded and consumed: a tile's loads
+    // are in flight while the other tile is computed. The loads are
+    // unconditional (past the row they re-read its last key, unused), so
+    // that every path leaves them in the same order and each compute waits
+    // only for its own tile.
+    Tile ta, tb;
+    fetch(wave, ta);
+    for (int t = wave; t < ntile; t += 2 * NW) {
+        fetch(t + NW, tb);
+        compute(t, ta);
+        fetch(t + 2 * NW, ta);
+        if (t + NW < ntile) compute(t + NW, tb);
+    }
+    __syncthreads();
+
+    for (int q = 0; q < 2; ++q) {
+        const int64_t rq = r + q;
+        if (rq >= QB) break;
+        const int64_t row = bh * QB + rq;
+        const float* ls = srow[q];
+        float* so = scores + row * M;
+        auto load_pair = [&](int i) {
+            const int j = 2 * i;
+            return make_float2(j < M32 ? ls[j] : -1.0f, j + 1 < M32 ? ls[j + 1] : -1.0f);
+        };
+        sip_row<NT, 0>(row, load_pair, [&](int j, float v) { so[j] = v; }, H, QB, M, budget,
+                       seed, sampling, capmask, keepmask, rowinfo, counts, status, redd, redi,
+                       redu);
     }
 }
 
@@ -1491,18 +1745,19 @@ hipError_t launch_checked(F&& f) {
 }  // namespace
 
 hipError_t launch_mean_keys(const void* k, Dtype dt, int64_t BH, int64_t N, int d,
-                            float* kbar, int8_t* kq, int* kx, hipStream_t s) {
-    const int64_t chunks = BH * (N / kKvBlock) * (d / 4);
+                            float* kbar, int8_t* kq, int8_t* kqt, int* kx, hipStream_t s) {
+    const int64_t M = N / kKvBlock;
+    const int64_t chunks = BH * M * (d / 4);
     const int threads = 256;                    // a multiple of d/4: blocks never straddle
     const int64_t blocks = (chunks + threads - 1) / threads;
     if (blocks == 0) return hipSuccess;
     return launch_checked([&] {
         if (dt == kBF16)
             hipLaunchKernelGGL(mean_keys_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const uint16_t*>(k), kbar, kq, kx, chunks, d);
+                               static_cast<const uint16_t*>(k), kbar, kq, kqt, kx, chunks, M, d);
         else
             hipLaunchKernelGGL(mean_keys_kernel<float>, dim3(blocks), dim3(threads), 0, s,
-                               static_cast<const float*>(k), kbar, kq, kx, chunks, d);
+                               static_cast<const float*>(k), kbar, kq, kqt, kx, chunks, M, d);
     });
 }
 
@@ -1561,7 +1816,7 @@ int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C) {
 template <int CP, int D>
 static void launch_scores_cpd(const float* cent, const float* w, const int8_t* kq,
                               const int* kx, int64_t BH, int64_t QB, int64_t M, int C,
-                              float2* part, float* scores, hipStream_t s) {
+                              float2* part, float* scores, bool pass2, hipStream_t s) {
     constexpr int rows_per_wg = kScoreWaves * (32 / CP);
     int chunk_tiles = 0, nchunks = 0;
     score_chunks(score_groups(BH, QB, C), M, &chunk_tiles, &nchunks);
@@ -1570,29 +1825,55 @@ static void launch_scores_cpd(const float* cent, const float* w, const int8_t* k
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((scores_kernel<CP, D, false>), grid, dim3(256), 0, s, cent, w, kq, kx, QB,
                        M, C, chunk_tiles, nchunks, scale_log2, part, scores);
-    hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kq, kx, QB,
-                       M, C, chunk_tiles, nchunks, scale_log2, part, scores);
+    if (pass2)
+        hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kq, kx,
+                           QB, M, C, chunk_tiles, nchunks, scale_log2, part, scores);
 }
 
 template <int CP>
 static void launch_scores_cp(const float* cent, const float* w, const int8_t* kq, const int* kx,
                              int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
-                             float* scores, hipStream_t s) {
+                             float* scores, bool pass2, hipStream_t s) {
     if (d == 128)
-        launch_scores_cpd<CP, 128>(cent, w, kq, kx, BH, QB, M, C, part, scores, s);
+        launch_scores_cpd<CP, 128>(cent, w, kq, kx, BH, QB, M, C, part, scores, pass2, s);
     else
-        launch_scores_cpd<CP, 64>(cent, w, kq, kx, BH, QB, M, C, part, scores, s);
+        launch_scores_cpd<CP, 64>(cent, w, kq, kx, BH, QB, M, C, part, scores, pass2, s);
 }
 
 hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
                          int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
-                         float* scores, hipStream_t s) {
+                         float* scores, bool pass2, hipStream_t s) {
     return launch_checked([&] {
-        if (C <= 1) launch_scores_cp<1>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 2) launch_scores_cp<2>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 4) launch_scores_cp<4>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
-        else if (C <= 8) launch_scores_cp<8>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
-        else launch_scores_cp<16>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, s);
+        if (C <= 1) launch_scores_cp<1>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+        else if (C <= 2) launch_scores_cp<2>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+        else if (C <= 4) launch_scores_cp<4>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+        else if (C <= 8) launch_scores_cp<8>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+        else launch_scores_cp<16>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+    });
+}
+
+hipError_t launch_scores_sip(const float* cent, const float* w, const int8_t* kqt, const int* kx,
+                             const float2* part, int64_t B, int64_t H, int64_t QB, int64_t M,
+                             int d, int C, int64_t budget, uint64_t seed, int sampling,
+                             float* scores, uint64_t* capmask, uint64_t* keepmask,
+                             SipRow* rowinfo, int64_t* counts, PlanStatus* status,
+                             hipStream_t s) {
+    if (C < 1 || C > 8 || M > kFusedMaxBlocks || (d != 64 && d != 128)) return hipErrorInvalidValue;
+    // the chunking of pass 1's statistics (the same grid as launch_scores)
+    int chunk_tiles = 0, nchunks = 0;
+    score_chunks(score_groups(B * H, QB, C), M, &chunk_tiles, &nchunks);
+    const dim3 grid(static_cast<unsigned>((QB + 1) / 2), static_cast<unsigned>(B * H));
+    return launch_checked([&] {
+        if (d == 128)
+            hipLaunchKernelGGL(scores_sip_kernel<128>, grid, dim3(kFusedThreads), 0, s, cent, w,
+                               kqt, kx, part, H, QB, M, C, nchunks,
+                               kLog2e / sqrtf(128.0f), budget, seed, sampling, scores, capmask,
+                               keepmask, rowinfo, counts, status);
+        else
+            hipLaunchKernelGGL(scores_sip_kernel<64>, grid, dim3(kFusedThreads), 0, s, cent, w,
+                               kqt, kx, part, H, QB, M, C, nchunks,
+                               kLog2e / sqrtf(64.0f), budget, seed, sampling, scores, capmask,
+                               keepmask, rowinfo, counts, status);
     });
 }
 

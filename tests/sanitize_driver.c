@@ -55,6 +55,21 @@ int main(void) {
     p.sampling = 7;
     expect("create sampling", absa_plan_create(fake, fake, ABSA_BF16, 1, 1, 1024, 64, &p, NULL, &plan),
            ABSA_ERR_INVALID_ARG);
+    p.sampling = ABSA_SAMPLING_POISSON;
+    p.fused = 1;
+    p.n_clusters = 12;
+    expect("create fused clusters", absa_plan_create(fake, fake, ABSA_BF16, 1, 1, 1024, 64, &p, NULL, &plan),
+           ABSA_ERR_UNSUPPORTED);
+    p.n_clusters = 8;
+    expect("create fused long rows", absa_plan_create(fake, fake, ABSA_BF16, 1, 1, 4 * 20228, 64, &p,
+                                                      NULL, &plan),
+           ABSA_ERR_UNSUPPORTED);
+    p.keep_intermediates = 1;
+    expect("create fused intermediates", absa_plan_create(fake, fake, ABSA_BF16, 1, 1, 1024, 64, &p,
+                                                          NULL, &plan),
+           ABSA_ERR_UNSUPPORTED);
+    p.keep_intermediates = 0;
+    p.fused = 0;
     if (plan != NULL) { fprintf(stderr, "a rejected call returned a plan\n"); ++failures; }
 
     /* plan_from_scores */

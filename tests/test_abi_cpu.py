@@ -63,7 +63,32 @@ def test_params_init_defaults():
     p = absa._Params()
     assert lib.absa_plan_params_init(ctypes.byref(p)) == 0
     assert (p.query_block, p.kv_block, p.n_clusters, p.kmeans_iters) == (128, 4, 8, 4)
+    assert (p.keep_intermediates, p.sampling, p.fused) == (0, 0, 0)
     assert lib.absa_plan_params_init(None) == absa.ABSA_ERR_INVALID_ARG
+
+
+def test_params_struct_matches_header():
+    """The binding's params struct has the C layout (size and field offsets
+    as the compiler lays out include/absa.h)."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in absa._Params._fields_]
+    body = "".join(f'printf("%zu ", offsetof(absa_plan_params, {f}));' for f in fields)
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "absa.h"\n'
+           f'int main(void){{{body} printf("%zu", sizeof(absa_plan_params)); return 0;}}\n')
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "layout.c")
+        exe = os.path.join(tmp, "layout")
+        open(c, "w").write(src)
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    want = [getattr(absa._Params, f).offset for f in fields] + [ctypes.sizeof(absa._Params)]
+    assert got == want
 
 
 _FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: every call below fails validation
@@ -106,6 +131,11 @@ def _create(**kw):
     (dict(kmeans_iters=0), absa.ABSA_ERR_INVALID_ARG),
     (dict(sampling=2), absa.ABSA_ERR_INVALID_ARG),
     (dict(sampling=-1), absa.ABSA_ERR_INVALID_ARG),
+    # the fused plan path: at most 8 clusters, rows of at most 20,224 blocks,
+    # no retained intermediates
+    (dict(fused=1, n_clusters=9), absa.ABSA_ERR_UNSUPPORTED),
+    (dict(fused=1, N=4 * 20225, budget_blocks=10), absa.ABSA_ERR_UNSUPPORTED),
+    (dict(fused=1, keep_intermediates=1), absa.ABSA_ERR_UNSUPPORTED),
 ])
 def test_plan_create_rejects(kw, status):
     assert _create(**kw) == status

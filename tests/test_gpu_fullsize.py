@@ -134,6 +134,26 @@ def test_plan_reuse_full_size(layer):
     assert len(L["o3_rows"]) >= 3
 
 
+def test_fused_plan_full_size(layer):
+    """The fused plan path at the layer's full size: bit-identical to the
+    two-pass plan (both designs) where the rows fit on chip (Wan2.1-like,
+    18,900 blocks); rows longer than 20,224 blocks (HunyuanVideo-like) are
+    refused."""
+    L = layer
+    qd, kd = L["q"].to(DEV), L["k"].to(DEV)
+    if L["M"] > 20224:
+        with pytest.raises(absa.AbsaError, match="UNSUPPORTED"):
+            absa.absa_plan_create(qd, kd, L["budget"], L["seed"], fused=True)
+        return
+    for sampling, ref in (("poisson", L["gp"]), ("systematic", L["gp_sys"])):
+        plan = absa.absa_plan_create(qd, kd, L["budget"], L["seed"], sampling=sampling,
+                                     fused=True)
+        gp = plan.export()
+        plan.destroy()
+        for key in ref:
+            assert np.array_equal(ref[key], gp[key]), (sampling, key)
+
+
 def test_whole_plan_properties(layer):
     L = layer
     gp = L["gp"]
