@@ -67,6 +67,8 @@ def parse():
                     help="run one 1 GiB device copy first (counter calibration)")
     ap.add_argument("--sampling", default="poisson", choices=["poisson", "systematic"],
                     help="sampling design of the plan (default poisson)")
+    ap.add_argument("--fused-plan", action="store_true",
+                    help="build the timed steps' plans with the fused score + SIP kernel")
     ap.add_argument("--sampling-study", action="store_true",
                     help="design comparison instead of the benchmark line: small video-shaped "
                          "layer, budgets 5/10/20%%, 8 seeds each, Poisson against systematic "
@@ -658,6 +660,23 @@ def schedule_run(workloads=("wan", "hunyuan"), steps=50, dense_first=10, every=4
           "note": "all-dense total = steps x the mean measured dense step"}, out_path)
 
 
+FUSED_MAX_BLOCKS = 20224     # the longest row (KV blocks) the fused plan kernel takes
+
+
+def fused_plan_entry(torch, absa, q, k, budget, seed, reps=5):
+    """Plan build time with the fused score pass 2 + SIP kernel against the
+    two-pass build, and whether the two plans are identical."""
+    two_ms, two = _plan_ms(torch, absa, q, k, budget, seed, reps=reps)
+    one_ms, one = _plan_ms(torch, absa, q, k, budget, seed, reps=reps, fused=True)
+    a, b = two.export(), one.export()
+    same = all(np.array_equal(a[key], b[key]) for key in a)
+    two.destroy()
+    one.destroy()
+    return {"plan_ms_two_pass": round(two_ms, 4), "plan_ms_fused": round(one_ms, 4),
+            "fused_over_two_pass": round(one_ms / two_ms, 3), "bitwise_equal_plan": bool(same),
+            "note": "wall time of absa_plan_create (it synchronises), median of 5"}
+
+
 def other_configs(torch, absa, timed, main_inputs, main_pct):
     """Per-layer figures of the other workloads and the Wan-shape reuse."""
     import synth
@@ -755,7 +774,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        plan = absa.absa_plan_create(qd, kd, budget, seed, sampling=args.sampling)
+        plan = absa.absa_plan_create(qd, kd, budget, seed, sampling=args.sampling,
+                                     fused=args.fused_plan)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -835,6 +855,10 @@ def main():
             "rel_l2_vs_dense": round(rel_l2_vs_dense, 6) if rel_l2_vs_dense is not None else None,
             "note": "the timed steps above"}}
         configs.update(other_configs(torch, absa, timed, (qd, kd, vd), pct))
+        if M <= FUSED_MAX_BLOCKS:
+            configs[f"{name}_{pct}_fused_plan"] = fused_plan_entry(torch, absa, qd, kd, budget,
+                                                                    seed)
+            print("[bench] config fused plan done", file=sys.stderr, flush=True)
 
     rec = {
         "metric": METRIC,
@@ -852,7 +876,9 @@ def main():
         "config": {"workload": WORKLOADS[name] if pct == cfg["budget_pct"]
                    else WORKLOADS[name].rsplit(",", 1)[0] + f", budget {pct}%",
                    "B": B, "H": H, "N": N, "d": d, "budget_blocks": budget,
-                   "sampling": args.sampling, "parallelism": "single GPU"},
+                   "sampling": args.sampling,
+                   "plan_kernels": "fused score pass 2 + SIP" if args.fused_plan else "two-pass",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sparse_attn_ms": round(attn_ms, 4),

@@ -1440,6 +1440,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
     float* __restrict__ scores, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     constexpr int NT = kFusedThreads;
+    // register-resident pairs per thread in the SIP phase: rows up to
+    // 2 NT kFusedSipPairs blocks (kFusedMaxBlocks fits)
+    constexpr int kFusedSipPairs = 10;
+    static_assert(2 * NT * kFusedSipPairs >= kFusedMaxBlocks, "fused rows fit the SIP registers");
     constexpr int NSTEP = D / 64;                   // MFMA k-steps (64 channels each)
     constexpr int NW = NT / 64;
     typedef int intx4 __attribute__((ext_vector_type(4)));
@@ -1591,7 +1595,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
             const int j = 2 * i;
             return make_float2(j < M32 ? ls[j] : -1.0f, j + 1 < M32 ? ls[j + 1] : -1.0f);
         };
-        sip_row<NT, 0>(row, load_pair, [&](int j, float v) { so[j] = v; }, H, QB, M, budget,
+        sip_row<NT, kFusedSipPairs>(row, load_pair, [&](int j, float v) { so[j] = v; }, H, QB, M, budget,
                        seed, sampling, capmask, keepmask, rowinfo, counts, status, redd, redi,
                        redu);
     }

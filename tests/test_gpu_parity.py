@@ -138,6 +138,19 @@ def test_plan_create_stages_and_output(case):
     check_output(to64(out), ref, "sparse (own plan)")
 
 
+@pytest.mark.parametrize("sampling", ["poisson", "systematic"])
+def test_fused_plan_on_parity_cases(case, sampling):
+    """The fused score pass 2 + SIP kernel gives the two-pass plan bit for
+    bit on every parity case (all fit its row limit)."""
+    c = case
+    seed = synth.sip_seed(4)
+    two = absa.absa_plan_create(c["q"], c["k"], c["budget"], seed, sampling=sampling).export()
+    one = absa.absa_plan_create(c["q"], c["k"], c["budget"], seed, sampling=sampling,
+                                fused=True).export()
+    for key in two:
+        assert np.array_equal(two[key], one[key]), (c["name"], sampling, key)
+
+
 def test_plan_create_systematic_end_to_end():
     """absa_plan_create with the fixed-size design: the plan is the oracle's
     systematic draw on the GPU's own scores (bit-exact), every row takes the
