@@ -154,7 +154,8 @@ absa_status absa_plan_params_init(absa_plan_params* out);
  * read the number of sampled blocks (the size of the plan's arrays, which
  * the host allocates), and once when the plan is complete (the build's
  * temporaries live in a per-device workspace that the next build reuses).
- * It returns with the plan complete, usable on any stream. */
+ * It returns with the plan complete, usable on any stream. B*H must not
+ * exceed 65535 (ABSA_ERR_UNSUPPORTED). */
 absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype,
                              int64_t B, int64_t H, int64_t N, int64_t d,
                              const absa_plan_params* params, void* hip_stream,

@@ -543,6 +543,10 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
     if (params->budget_blocks < 1 || params->budget_blocks > M)
         return fail(ABSA_ERR_INVALID_ARG, "budget_blocks must lie in [1, M=%lld] (got %lld)",
                     (long long)M, (long long)params->budget_blocks);
+    if (B * H > 65535)
+        return fail(ABSA_ERR_UNSUPPORTED,
+                    "absa_plan_create needs B*H <= 65535 (the score kernels' second grid "
+                    "dimension; got %lld)", (long long)(B * H));
     const bool fused = params->fused != 0;
     if (fused && (params->n_clusters > 8 || M > kFusedMaxBlocks || params->keep_intermediates))
         return fail(ABSA_ERR_UNSUPPORTED,

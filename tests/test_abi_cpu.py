@@ -136,6 +136,8 @@ def _create(**kw):
     (dict(fused=1, n_clusters=9), absa.ABSA_ERR_UNSUPPORTED),
     (dict(fused=1, N=4 * 20225, budget_blocks=10), absa.ABSA_ERR_UNSUPPORTED),
     (dict(fused=1, keep_intermediates=1), absa.ABSA_ERR_UNSUPPORTED),
+    # the score kernels put B*H on the grid's second dimension
+    (dict(B=2, H=40000, N=128, budget_blocks=1), absa.ABSA_ERR_UNSUPPORTED),
 ])
 def test_plan_create_rejects(kw, status):
     assert _create(**kw) == status
