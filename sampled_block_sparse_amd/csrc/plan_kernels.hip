@@ -1595,9 +1595,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
             const int j = 2 * i;
             return make_float2(j < M32 ? ls[j] : -1.0f, j + 1 < M32 ? ls[j + 1] : -1.0f);
         };
-        sip_row<NT, kFusedSipPairs>(row, load_pair, [&](int j, float v) { so[j] = v; }, H, QB, M, budget,
-                       seed, sampling, capmask, keepmask, rowinfo, counts, status, redd, redi,
-                       redu);
+        sip_row<NT, kFusedSipPairs>(row, load_pair, [&](int j, float v) { so[j] = v; }, H, QB,
+                                    M, budget, seed, sampling, capmask, keepmask, rowinfo,
+                                    counts, status, redd, redi, redu);
     }
 }
 
