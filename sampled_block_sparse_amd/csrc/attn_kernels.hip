@@ -11,7 +11,8 @@
 //             into full tensor-core tiles at no extra matrix-core cost).
 //
 // Design (one workgroup = one plan row = 128 queries of one (b, h); 4 waves,
-// wave w owns queries [32w, 32w+32)):
+// wave w owns queries [32w, 32w+32); the dense comparator takes two
+// neighbouring rows of a head per workgroup of 8 waves, sharing their tiles):
 //   * A key tile is 16 KV blocks = 64 keys. The 16 blocks of a tile are the
 //     row's next 16 plan entries; each is 4 consecutive tokens, i.e. one
 //     contiguous 4*d*2-byte piece of K and of V, so the gather is a set of
@@ -156,13 +157,24 @@ __device__ __forceinline__ void load_to_lds(const char* base, uint32_t off, uint
 }
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Rows per workgroup: the dense comparator runs two neighbouring query blocks
+// of a head in one workgroup of 8 waves, which need the same K/V tiles, so
+// each tile is gathered once for both (half the gather and HBM traffic per
+// query); every wave's own work is unchanged, so its output is the same bit
+// for bit. A sparse row has its own blocks: one row of 4 waves.
+template <bool DENSE> constexpr int kRowsPerGroup = DENSE ? 2 : 1;
+
 template <int D, bool OUT_F32, bool DENSE>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
+__global__ __launch_bounds__(256 * kRowsPerGroup<DENSE>, 2 / kRowsPerGroup<DENSE>) void attn_kernel(
+    AttnParams P) {
+    constexpr int RW = kRowsPerGroup<DENSE>;
+    constexpr int NW = 4 * RW;                  // waves per workgroup
     constexpr int NS = D / 16;                  // 16-channel MFMA steps
     constexpr int ND = D / 32;                  // 32-channel output blocks
     constexpr int ROWB = D * 2;                 // bytes of one bf16 key row
     constexpr uint32_t BLOCK_BYTES = kKvBlock * ROWB;
-    constexpr int CPW = kTileKeys * ROWB / 1024 / 4;   // 1 KB gather chunks per wave
+    constexpr int CPW = kTileKeys * ROWB / 1024 / NW;  // 1 KB gather chunks per wave
+    static_assert(CPW >= 1, "every wave gathers at least one chunk");
     constexpr int KPC = 1024 / ROWB;            // key rows per chunk
     // the two K buffers are one array, so a K operand address is one
     // loop-invariant register plus an immediate offset for buffer and key half
@@ -174,17 +186,22 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     auto Vbuf = [&](auto b) -> uint16_t* { if constexpr (decltype(b)::value) return Vs1; else return Vs0; };
     auto Lbuf = [&](auto b) -> float* { if constexpr (decltype(b)::value) return lws1; else return lws0; };
 
+    // Work unit = RW consecutive query blocks of one head (a row, or a pair
+    // of rows; with an odd QB the last pair has one real row and the second
+    // half computes on no queries).
     const int bid = blockIdx.x;
-    const int64_t row = static_cast<int64_t>(bid % kXcds) * P.per_xcd + bid / kXcds;
-    if (row >= P.rows) return;
+    const int64_t unit = static_cast<int64_t>(bid % kXcds) * P.per_xcd + bid / kXcds;
+    const int64_t units_per_head = (P.QB + RW - 1) / RW;
+    if (unit >= P.rows / P.QB * units_per_head) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
 
-    const int64_t bh = row / P.QB;
-    const int64_t r = row - bh * P.QB;
+    const int64_t bh = unit / units_per_head;
+    const int64_t r = (unit - bh * units_per_head) * RW + wave / 4;   // this wave's query block
+    const int64_t row = bh * P.QB + r;          // its plan row (sparse: RW = 1, r < QB)
     const int64_t q0 = r * kQueryBlock;
     const int64_t head_off = bh * P.N * D;
     const char* kbase = static_cast<const char*>(P.k) + head_off * 2;
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
     const int ntiles = (cnt32 + kTileBlocks - 1) / kTileBlocks;
 
     // ---- the wave's queries as the B operand of S^T = K Q^T ----
-    const int64_t my_q = q0 + wave * 32 + col;
+    const int64_t my_q = q0 + (wave & 3) * 32 + col;
     bf16x8 qb[NS];
     {
         const bool ok = my_q < P.N;
@@ -556,9 +573,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams P) {
 
 template <int D, bool OUT_F32, bool DENSE>
 void launch_one(const AttnParams& p, hipStream_t s) {
-    const int64_t grid = p.per_xcd * kXcds;
+    constexpr int RW = kRowsPerGroup<DENSE>;
+    const int64_t units = p.rows / p.QB * ((p.QB + RW - 1) / RW);
+    AttnParams q = p;
+    q.per_xcd = (units + kXcds - 1) / kXcds;
+    const int64_t grid = q.per_xcd * kXcds;
     hipLaunchKernelGGL((attn_kernel<D, OUT_F32, DENSE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(256), 0, s, p);
+                       dim3(256 * RW), 0, s, q);
 }
 
 // fp32 -> bf16, round to nearest even; 8 elements per thread and iteration.
