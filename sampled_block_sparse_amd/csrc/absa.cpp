@@ -316,6 +316,7 @@ struct PlanTemps {
     float* w = nullptr;
     float* scores = nullptr;
     float2* part = nullptr;
+    float* sbias = nullptr;      // score bias per (query block, centroid)
     uint64_t* capmask = nullptr;
     uint64_t* keepmask = nullptr;
     SipRow* rowinfo = nullptr;
@@ -390,7 +391,7 @@ absa_status run_sip(absa_plan_s* P, const float* scores, int64_t budget, uint64_
     ABSA_TRY(arena.alloc(&P->rowptr, rows + 1, "row pointers"));
     ABSA_HIP(hipMemsetAsync(t.status, 0, sizeof(PlanStatus), s), "clear plan status");
     if (fused)
-        ABSA_HIP(launch_scores_sip(t.cent, t.w, t.kqt, t.kx, t.part, P->B, P->H, P->QB, P->M,
+        ABSA_HIP(launch_scores_sip(t.cent, t.w, t.kqt, t.kx, t.sbias, P->B, P->H, P->QB, P->M,
                                    static_cast<int>(P->d), P->n_clusters, budget, seed, sampling,
                                    t.scores, t.capmask, t.keepmask, t.rowinfo, t.counts, t.status,
                                    s),
@@ -581,6 +582,7 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
                                  "tile-major mean-key digits"));
             ABSA_TRY(a.alloc(&t.kx, B * H * M, "mean-key exponents"));
             ABSA_TRY(a.alloc(&t.part, score_partials(B * H, P->QB, M, C), "score chunk statistics"));
+            ABSA_TRY(a.alloc(&t.sbias, P->rows * C, "score biases"));
             return sip_temps(a, P, t);
         };
         PlanTemps t;
@@ -611,7 +613,7 @@ absa_status absa_plan_create(const void* q, const void* k, absa_dtype dtype, int
                  "k-means kernel");
         ABSA_TRY(fork.join());
         ABSA_HIP(launch_scores(t.cent, t.w, t.kq, t.kx, B * H, P->QB, M, static_cast<int>(d), C,
-                               t.part, t.scores, !fused, s),
+                               t.part, t.sbias, t.scores, !fused, s),
                  "score kernel");
         ABSA_TRY(run_sip(P, t.scores, params->budget_blocks, params->seed, params->sampling, s,
                          arena, t, fused));

@@ -54,21 +54,22 @@ hipError_t launch_kmeans(const void* q, Dtype dt, int64_t BH, int64_t N, int d,
 // argument of launch_scores).
 int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C);
 
-// Both score passes, or (pass2 = false) pass 1 alone, whose chunk
-// statistics launch_scores_sip takes.
+// Pass 1 (chunk statistics into part), the bias of every (query block,
+// centroid) from them (sbias, float [BH*QB*C]), then pass 2 (scores) unless
+// pass2 = false (the fused kernel takes sbias instead).
 hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
                          int64_t BH, int64_t QB, int64_t M, int d, int C,
-                         float2* part, float* scores, bool pass2, hipStream_t s);
+                         float2* part, float* sbias, float* scores, bool pass2, hipStream_t s);
 
 // Score pass 2 fused with the SIP count: the same outputs as pass 2 and
 // launch_sip_count, except that scores receives only the scores the fill
 // kernel reads (kept blocks that are not capped). Needs C <= 8 and
-// M <= kFusedMaxBlocks; part from launch_scores(..., pass2 = false), kqt
+// M <= kFusedMaxBlocks; sbias from launch_scores(..., pass2 = false), kqt
 // from launch_mean_keys.
 constexpr int kFusedThreads = 1024;
 constexpr int64_t kFusedMaxBlocks = 20224;
 hipError_t launch_scores_sip(const float* cent, const float* w, const int8_t* kqt, const int* kx,
-                             const float2* part, int64_t B, int64_t H, int64_t QB, int64_t M,
+                             const float* sbias, int64_t B, int64_t H, int64_t QB, int64_t M,
                              int d, int C, int64_t budget, uint64_t seed, int sampling,
                              float* scores, uint64_t* capmask, uint64_t* keepmask,
                              SipRow* rowinfo, int64_t* counts, PlanStatus* status,

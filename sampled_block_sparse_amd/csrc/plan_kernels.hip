@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace absa {
 namespace {
 
@@ -439,6 +441,21 @@ __device__ __forceinline__ float score_bias(const float2* __restrict__ part,
     return (wm > 0.0f) ? log2f(wm / z) - mx : -INFINITY;
 }
 
+// The bias of every (query block, centroid), computed once between the
+// passes: with the keys split into chunks, every pass-2 workgroup would
+// otherwise recombine all chunks' statistics for each of its slots.
+__global__ __launch_bounds__(256) void score_bias_kernel(const float2* __restrict__ part,
+                                                         const float* __restrict__ w, int64_t QB,
+                                                         int C, int nchunks, int64_t n,
+                                                         float* __restrict__ sbias) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t rc = i / C;
+    const int m = static_cast<int>(i - rc * C);
+    const int64_t bh = rc / QB;
+    sbias[i] = score_bias(part, w, bh, QB, C, nchunks, rc - bh * QB, m);
+}
+
 // The score contraction of one head runs in two passes over key chunks, so
 // the grid has (query-block groups) x (heads) x (chunks) workgroups and
 // fills the chip whatever the head count. Pass 1 (PASS2 = false) writes, per centroid and chunk, the running
@@ -454,6 +471,7 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
                                                         int chunk_tiles, int nchunks,
                                                         float scale_log2,
                                                         float2* __restrict__ part,
+                                                        const float* __restrict__ sbias,
                                                         float* __restrict__ scores) {
     constexpr int RPW = 32 / CP;                    // query blocks per wave
     constexpr int NSTEP = D / 32;                   // MFMA k-steps (32 channels each)
@@ -780,15 +798,15 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const float* __restrict_
             }
         }
     } else {
-        // Reference and sum of each centroid over all chunks, in chunk
-        // order, folded with the centroid's weight into one exponent bias:
-        // w_m * 2^(x - R) / Z = 2^(x + log2(w_m / Z) - R); -inf for unused
-        // slots (weight 0).
+        // Each centroid's exponent bias (score_bias, computed once per
+        // centroid by score_bias_kernel): w_m * 2^(x - R) / Z =
+        // 2^(x + log2(w_m / Z) - R); -inf for unused slots (weight 0).
         float bias[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int slot = slot_of(i);
-            bias[i] = score_bias(part, w, bh, QB, C, nchunks, r0 + slot / CP, slot % CP);
+            bias[i] = slot_valid(slot) ? sbias[(bh * QB + r0 + slot / CP) * C + slot % CP]
+                                       : -INFINITY;
         }
         float pr[RPW];
         auto item = [&](const intx16& i22, const intx16& i21, const intx16& i20,
@@ -1435,8 +1453,8 @@ __global__ __launch_bounds__(NT, (MAXP > 0 && MAXP <= 20) ? 6 : 4) void sip_coun
 template <int D>
 __global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
     const float* __restrict__ cent, const float* __restrict__ w, const int8_t* __restrict__ kqt,
-    const int* __restrict__ kx, const float2* __restrict__ part, int64_t H, int64_t QB, int64_t M,
-    int C, int nchunks, float scale_log2, int64_t budget, uint64_t seed, int sampling,
+    const int* __restrict__ kx, const float* __restrict__ sbias, int64_t H, int64_t QB, int64_t M,
+    int C, float scale_log2, int64_t budget, uint64_t seed, int sampling,
     float* __restrict__ scores, uint64_t* __restrict__ capmask, uint64_t* __restrict__ keepmask,
     SipRow* __restrict__ rowinfo, int64_t* __restrict__ counts, PlanStatus* __restrict__ status) {
     constexpr int NT = kFusedThreads;
@@ -1519,8 +1537,11 @@ __global__ __launch_bounds__(kFusedThreads, 1) void scores_sip_kernel(
     // clusters 4 ((lane / 16) % 2) + i
     float bias[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        bias[i] = score_bias(part, w, bh, QB, C, nchunks, r + (lane >> 5), 4 * ((lane >> 4) & 1) + i);
+    for (int i = 0; i < 4; ++i) {
+        const int64_t rb = r + (lane >> 5);
+        const int mb = 4 * ((lane >> 4) & 1) + i;
+        bias[i] = (rb < QB && mb < C) ? sbias[(bh * QB + rb) * C + mb] : -INFINITY;
+    }
 
     const int ntile = (M32 + 15) / 16;
     const int8_t* kt = kqt + bh * ntile * (3 * D * 16) + lane * 16;
@@ -1820,7 +1841,8 @@ int64_t score_partials(int64_t BH, int64_t QB, int64_t M, int C) {
 template <int CP, int D>
 static void launch_scores_cpd(const float* cent, const float* w, const int8_t* kq,
                               const int* kx, int64_t BH, int64_t QB, int64_t M, int C,
-                              float2* part, float* scores, bool pass2, hipStream_t s) {
+                              float2* part, float* sbias, float* scores, bool pass2,
+                              hipStream_t s) {
     constexpr int rows_per_wg = kScoreWaves * (32 / CP);
     int chunk_tiles = 0, nchunks = 0;
     score_chunks(score_groups(BH, QB, C), M, &chunk_tiles, &nchunks);
@@ -1828,56 +1850,58 @@ static void launch_scores_cpd(const float* cent, const float* w, const int8_t* k
                     static_cast<unsigned>(BH), static_cast<unsigned>(nchunks));
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((scores_kernel<CP, D, false>), grid, dim3(256), 0, s, cent, w, kq, kx, QB,
-                       M, C, chunk_tiles, nchunks, scale_log2, part, scores);
+                       M, C, chunk_tiles, nchunks, scale_log2, part, sbias, scores);
+    const int64_t nb = BH * QB * C;
+    hipLaunchKernelGGL(score_bias_kernel, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256),
+                       0, s, part, w, QB, C, nchunks, nb, sbias);
     if (pass2)
         hipLaunchKernelGGL((scores_kernel<CP, D, true>), grid, dim3(256), 0, s, cent, w, kq, kx,
-                           QB, M, C, chunk_tiles, nchunks, scale_log2, part, scores);
+                           QB, M, C, chunk_tiles, nchunks, scale_log2, part, sbias, scores);
 }
 
 template <int CP>
 static void launch_scores_cp(const float* cent, const float* w, const int8_t* kq, const int* kx,
                              int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
-                             float* scores, bool pass2, hipStream_t s) {
+                             float* sbias, float* scores, bool pass2, hipStream_t s) {
     if (d == 128)
-        launch_scores_cpd<CP, 128>(cent, w, kq, kx, BH, QB, M, C, part, scores, pass2, s);
+        launch_scores_cpd<CP, 128>(cent, w, kq, kx, BH, QB, M, C, part, sbias, scores, pass2, s);
     else
-        launch_scores_cpd<CP, 64>(cent, w, kq, kx, BH, QB, M, C, part, scores, pass2, s);
+        launch_scores_cpd<CP, 64>(cent, w, kq, kx, BH, QB, M, C, part, sbias, scores, pass2, s);
 }
 
 hipError_t launch_scores(const float* cent, const float* w, const int8_t* kq, const int* kx,
                          int64_t BH, int64_t QB, int64_t M, int d, int C, float2* part,
-                         float* scores, bool pass2, hipStream_t s) {
+                         float* sbias, float* scores, bool pass2, hipStream_t s) {
     return launch_checked([&] {
-        if (C <= 1) launch_scores_cp<1>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
-        else if (C <= 2) launch_scores_cp<2>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
-        else if (C <= 4) launch_scores_cp<4>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
-        else if (C <= 8) launch_scores_cp<8>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
-        else launch_scores_cp<16>(cent, w, kq, kx, BH, QB, M, d, C, part, scores, pass2, s);
+        auto go = [&](auto cp) {
+            launch_scores_cp<decltype(cp)::value>(cent, w, kq, kx, BH, QB, M, d, C, part, sbias,
+                                                  scores, pass2, s);
+        };
+        if (C <= 1) go(std::integral_constant<int, 1>{});
+        else if (C <= 2) go(std::integral_constant<int, 2>{});
+        else if (C <= 4) go(std::integral_constant<int, 4>{});
+        else if (C <= 8) go(std::integral_constant<int, 8>{});
+        else go(std::integral_constant<int, 16>{});
     });
 }
 
 hipError_t launch_scores_sip(const float* cent, const float* w, const int8_t* kqt, const int* kx,
-                             const float2* part, int64_t B, int64_t H, int64_t QB, int64_t M,
+                             const float* sbias, int64_t B, int64_t H, int64_t QB, int64_t M,
                              int d, int C, int64_t budget, uint64_t seed, int sampling,
                              float* scores, uint64_t* capmask, uint64_t* keepmask,
                              SipRow* rowinfo, int64_t* counts, PlanStatus* status,
                              hipStream_t s) {
     if (C < 1 || C > 8 || M > kFusedMaxBlocks || (d != 64 && d != 128)) return hipErrorInvalidValue;
-    // the chunking of pass 1's statistics (the same grid as launch_scores)
-    int chunk_tiles = 0, nchunks = 0;
-    score_chunks(score_groups(B * H, QB, C), M, &chunk_tiles, &nchunks);
     const dim3 grid(static_cast<unsigned>((QB + 1) / 2), static_cast<unsigned>(B * H));
     return launch_checked([&] {
         if (d == 128)
             hipLaunchKernelGGL(scores_sip_kernel<128>, grid, dim3(kFusedThreads), 0, s, cent, w,
-                               kqt, kx, part, H, QB, M, C, nchunks,
-                               kLog2e / sqrtf(128.0f), budget, seed, sampling, scores, capmask,
-                               keepmask, rowinfo, counts, status);
+                               kqt, kx, sbias, H, QB, M, C, kLog2e / sqrtf(128.0f), budget, seed,
+                               sampling, scores, capmask, keepmask, rowinfo, counts, status);
         else
             hipLaunchKernelGGL(scores_sip_kernel<64>, grid, dim3(kFusedThreads), 0, s, cent, w,
-                               kqt, kx, part, H, QB, M, C, nchunks,
-                               kLog2e / sqrtf(64.0f), budget, seed, sampling, scores, capmask,
-                               keepmask, rowinfo, counts, status);
+                               kqt, kx, sbias, H, QB, M, C, kLog2e / sqrtf(64.0f), budget, seed,
+                               sampling, scores, capmask, keepmask, rowinfo, counts, status);
     });
 }
 
