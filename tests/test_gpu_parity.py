@@ -39,6 +39,10 @@ CASES = {
     # bf16 output at d = 64 over several key tiles (75 blocks: 5 tiles, the
     # last one partial) and a partial last query block
     "multi_d64_bf16": (dict(B=1, H=2, N=3000, d=64, seed=23), ("pct", 10)),
+    # two batches with an odd number of query blocks per head (11): the
+    # dense comparator's last two-block workgroup of every head holds one
+    # real block, and the fused plan kernel's last pair has one row
+    "batch2_odd_qb": (dict(B=2, H=2, N=1340, d=128, seed=29), ("pct", 10)),
 }
 
 
