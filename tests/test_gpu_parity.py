@@ -610,3 +610,54 @@ def test_multi_step_schedule_against_oracle():
         torch.cuda.synchronize()
         sub = oracle.OraclePlan(B, len(hs), N, d, N // 4, (N + 127) // 128, *_subplan(gp, H, hs, N))
         check_output(to64(out)[:, hs], oracle.plan_attention(Q, K, V, sub), f"sparse step {step}")
+
+
+def test_concurrent_builds_and_calls_match_sequential():
+    """Plans built concurrently from four host threads, each on its own
+    stream (the device workspace is held by one build at a time, the others
+    allocate their own; the mean-key side stream is shared), and attention
+    run concurrently on those streams, equal the same calls made one after
+    another, bit for bit."""
+    import threading
+    q, k, v = (x.to(DEV) for x in _inputs(B=1, H=8, N=4096, d=128, seed=37))
+    budget = 100
+    groups = [(2 * i, 2 * i + 2) for i in range(4)]
+
+    def sl(x, g):
+        return x[:, g[0]:g[1]]
+
+    ref_plans, ref_out = [], []
+    for i, g in enumerate(groups):
+        p = absa.absa_plan_create(sl(q, g), sl(k, g), budget, 50 + i)
+        ref_plans.append(p.export())
+        ref_out.append(absa.absa_sparse_attention(p, sl(q, g), sl(k, g), sl(v, g)))
+        p.destroy()
+    torch.cuda.synchronize()
+
+    streams = [torch.cuda.Stream() for _ in groups]
+    plans, outs = [None] * len(groups), [None] * len(groups)
+    errors = []
+
+    def work(i):
+        try:
+            g = groups[i]
+            p = absa.absa_plan_create(sl(q, g), sl(k, g), budget, 50 + i, stream=streams[i])
+            o = torch.empty_like(sl(q, g))
+            absa.absa_sparse_attention(p, sl(q, g), sl(k, g), sl(v, g), o, stream=streams[i])
+            plans[i], outs[i] = p, o
+        except Exception as e:      # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(groups))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(groups)):
+        gp = plans[i].export()
+        for key in gp:
+            assert np.array_equal(gp[key], ref_plans[i][key]), (i, key)
+        assert torch.equal(outs[i], ref_out[i]), i
+        plans[i].destroy()
