@@ -34,6 +34,9 @@ FUSED_CASES = [
     (1, 2, 2000, 128, "bf16", 5, 10, "systematic"),  # C = 5
     (1, 2, 8192, 128, "bf16", 8, 10, "poisson"),     # the small layer's shape
     (1, 1, 80896, 128, "bf16", 8, 10, "poisson"),    # M = 20224, the longest fused row
+    (1, 2, 1024, 128, "bf16", 8, 100, "systematic"),  # budget 100% under the fixed-size design
+    (1, 1, 4, 128, "bf16", 8, 100, "poisson"),       # N = 4: one KV block, one query block
+    (2, 1, 260, 64, "f32", 8, 50, "systematic"),     # QB = 3 per head: one lone row per head
 ]
 
 
